@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Workload: the Llama-3-8B-shaped decode layer in bf16 -- 64 requests with KV
+lengths uniform in [512, 4096], 32 query heads over 8 KV heads (GQA 4:1),
+head_dim 128, 16-token blocks, a pool 1.2x the blocks needed, shuffled block
+tables. One step = the slot_mapping write of the 64 new tokens' K/V plus paged
+GQA decode attention over every request's whole KV (split-K partials and the
+LSE merge when the step uses them).
+
+Inputs are synthetic and seeded, generated on the GPU, and resident in HBM
+before timing. Steps rotate over several independent copies of the inputs so
+no step finds the previous step's KV in the 256 MB last-level cache.
+
+Printed: one JSON line. ``value`` is the step's algorithmic HBM traffic
+divided by the step time (GB/s). ``roofline`` is for the attention kernel,
+timed with HIP events recorded on the stream it is launched on.
+``cpu_baseline`` is the fp64 CPU oracle on the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged GQA decode: achieved HBM GB/s (% of peak) + decode tokens/s per layer"
+PEAK_HBM_GBS = 8000.0
+ATTN_SOURCES = ["attention.hip", "attn_tile.h", "pa_api.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_221_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(layout) -> int:
+    """Bytes decode attention must move: every request's K and V, Q in and O
+    out, the block-table entries it follows and seq_lens."""
+    e = layout.elem_bytes
+    kvb = 2 * layout.num_kv_heads * layout.head_dim * e
+    bs = layout.block_size
+    lens = layout.seq_lens.astype("int64")
+    blocks = (lens + bs - 1) // bs
+    qo = 2 * layout.num_seqs * layout.num_heads * layout.head_dim * e
+    return int(lens.sum() * kvb + qo + 4 * blocks.sum() + 4 * layout.num_seqs)
+
+
+def write_bytes(layout) -> int:
+    """Bytes the KV write must move: read and write K+V rows, read slots."""
+    kvb = 2 * layout.num_kv_heads * layout.head_dim * layout.elem_bytes
+    return int(2 * layout.num_tokens * kvb + 8 * layout.num_tokens)
+
+
+def varlen_bytes(layout) -> int:
+    """Per-request KV bytes of a varlen step (each request reads its KV once)."""
+    e = layout.elem_bytes
+    kvb = 2 * layout.num_kv_heads * layout.head_dim * e
+    lens = layout.seq_lens.astype("int64")
+    qo = 2 * layout.num_tokens * layout.num_heads * layout.head_dim * e
+    blocks = (lens + layout.block_size - 1) // layout.block_size
+    return int(lens.sum() * kvb + qo + 4 * blocks.sum() + 4 * (2 * layout.num_seqs + 1))
+
+
+def load_traffic(src_hash: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != src_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+class DecodeStep:
+    """One step on one copy of the inputs: write, then attention."""
+
+    def __init__(self, st, path: str, split_tokens: int):
+        import torch
+        import paged_kv_cache_221_amd as pa
+        self.pa, self.torch = pa, torch
+        self.st, self.path, self.split = st, path, split_tokens
+        lay = st.layout
+        self.out = torch.empty_like(st.q)
+        if path == "splitk":
+            s = pa.pa_splitk_num_splits(lay.max_seq_len, split_tokens)
+            b, hq, d = st.q.shape
+            self.o_part = torch.empty((b, hq, s, d), dtype=torch.float32, device=st.q.device)
+            self.lse_part = torch.empty((b, hq, s), dtype=torch.float32, device=st.q.device)
+
+    def __call__(self, ev=None):
+        st, pa, lay = self.st, self.pa, self.st.layout
+        pa.pa_write_kv(st.k_cache, st.v_cache, st.k_new, st.v_new, st.slot_mapping)
+        if ev is not None:
+            ev[0].record()
+        if self.path == "decode":
+            pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                         lay.max_seq_len, lay.scale, out=self.out)
+            if ev is not None:
+                ev[1].record()
+        else:
+            pa.pa_decode_splitk(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                                lay.max_seq_len, self.split, lay.scale, o_part=self.o_part,
+                                lse_part=self.lse_part)
+            if ev is not None:
+                ev[1].record()
+            pa.pa_lse_merge(self.o_part, self.lse_part, st.seq_lens, lay.max_seq_len,
+                            self.split, out_dtype=st.q.dtype, out=self.out)
+
+
+def time_steps(steps_fns, k: int, w: int, kernel_events: bool):
+    """Eager timing: W warmup steps, K timed steps; optional per-kernel events."""
+    import torch
+    n = len(steps_fns)
+    for i in range(w):
+        steps_fns[i % n]()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(k)] if kernel_events else [None] * k
+    t0 = time.perf_counter()
+    for i in range(k):
+        steps_fns[i % n](evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = None
+    if kernel_events:
+        kern_ms = sum(a.elapsed_time(b) for a, b in evs) / k
+    return (t1 - t0) * 1e3 / k, kern_ms
+
+
+def time_graph(steps_fns, k: int, w: int):
+    """Graph timing: one captured HIP graph per input copy, replayed in turn."""
+    import torch
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in steps_fns:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for fn in steps_fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs.append(g)
+    n = len(graphs)
+    for i in range(w):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(k):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / k
+
+
+def cpu_baseline(st, layout, budget_s: float):
+    """The fp64 oracle on the whole step (write + decode of all requests),
+    repeated until ``budget_s`` of CPU time has been spent."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    from workloads.tensors import raw_bits
+    dt = layout.dtype
+    k0, v0 = raw_bits(st.k_cache, dt).copy(), raw_bits(st.v_cache, dt).copy()
+    q, kn, vn = raw_bits(st.q, dt), raw_bits(st.k_new, dt), raw_bits(st.v_new, dt)
+    reps, spent = 0, 0.0
+    while spent < budget_s or reps == 0:
+        t = time.perf_counter()
+        oracle.write_kv(k0, v0, kn, vn, layout.slot_mapping, layout.block_size)
+        oracle.paged_decode(q, k0, v0, layout.block_table, layout.seq_lens, layout.scale,
+                            layout.block_size, dt)
+        spent += time.perf_counter() - t
+        reps += 1
+    per_step = spent / reps
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    gbs = (decode_bytes(layout) + write_bytes(layout)) / per_step / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole step ({layout.num_seqs} requests, {int(layout.seq_lens.sum())} "
+                      f"KV tokens) repeated {reps}x, {per_step:.2f} s per step; numpy fp64 "
+                      f"with BLAS on {threads} threads; host cpu_count={os.cpu_count()}"}
+
+
+def secondary(args):
+    """Per-config attention timings on the other step shapes (not the metric)."""
+    import torch
+    import paged_kv_cache_221_amd as pa
+    from workloads import llama2_7b_mha_decode, long_context_splitk, mixed_step
+    from workloads.tensors import materialize
+    res = {}
+    k = max(3, min(args.steps, 10))
+    for name, fn in (("long-context-splitk-bf16", long_context_splitk),
+                     ("llama2-7b-mha-decode-fp16", llama2_7b_mha_decode),
+                     ("mixed-step-bf16", mixed_step)):
+        lay = fn()
+        st = materialize(lay, "cuda", poison=False)
+        if name.startswith("long"):
+            step = DecodeStep(st, "splitk", lay.split_tokens)
+            nbytes = decode_bytes(lay)
+        elif name.startswith("llama2"):
+            step = DecodeStep(st, "decode", 0)
+            nbytes = decode_bytes(lay)
+        else:
+            out = torch.empty_like(st.q)
+
+            def step(ev=None, st=st, lay=lay, out=out):
+                pa.pa_write_kv(st.k_cache, st.v_cache, st.k_new, st.v_new, st.slot_mapping)
+                if ev is not None:
+                    ev[0].record()
+                pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                             st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
+                             out=out)
+                if ev is not None:
+                    ev[1].record()
+            nbytes = varlen_bytes(lay)
+        ms, kern = time_steps([step], k, 2, True)
+        res[name] = {"step_ms": round(ms, 4), "attention_kernel_ms": round(kern, 4),
+                     "attention_GBps": round(nbytes / (kern * 1e-3) / 1e9, 1),
+                     "attention_frac_of_8TBps": round(nbytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": nbytes}
+        print(f"[bench] {name}: attention {kern:.4f} ms", file=sys.stderr, flush=True)
+        del st, step
+        torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--path", choices=["decode", "splitk"], default="decode")
+    ap.add_argument("--split-tokens", type=int, default=512)
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from paged_kv_cache_221_amd import _native
+    if not os.path.exists(_native.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import paged_kv_cache_221_amd as pa
+    from workloads import llama3_8b_decode
+    from workloads.tensors import materialize
+    pa.load()
+    torch.cuda.set_device(0)
+
+    layout = llama3_8b_decode()
+    copies = [materialize(layout, "cuda", seed_offset=i) for i in range(args.copies)]
+    steps = [DecodeStep(st, args.path, args.split_tokens) for st in copies]
+    print(f"[bench] {layout.name}: {layout.num_seqs} requests, "
+          f"{int(layout.seq_lens.sum())} KV tokens, path={args.path}", file=sys.stderr,
+          flush=True)
+
+    eager_ms, kern_ms = time_steps(steps, args.steps, args.warmup, True)
+    graph_ms = None if args.no_graph else time_graph(steps, args.steps, args.warmup)
+    step_ms = graph_ms if graph_ms is not None else eager_ms
+
+    dec_b, wr_b = decode_bytes(layout), write_bytes(layout)
+    step_bytes = dec_b + wr_b
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    achieved = dec_b / (kern_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(src_hash)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, generated on the GPU; no weights)",
+        "config": {"workload": layout.name, "num_seqs": layout.num_seqs,
+                   "seq_len_range": [512, 4096], "total_kv_tokens": int(layout.seq_lens.sum()),
+                   "num_heads": layout.num_heads, "num_kv_heads": layout.num_kv_heads,
+                   "head_dim": layout.head_dim, "block_size": layout.block_size,
+                   "num_blocks": layout.num_blocks, "path": args.path,
+                   "split_tokens": args.split_tokens if args.path == "splitk" else None,
+                   "input_copies": args.copies, "timing": "hip-graph" if graph_ms else "eager"},
+        "hbm_frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "decode_tokens_per_s_per_layer": round(layout.num_seqs / (step_ms * 1e-3), 1),
+        "eager_ms_per_step": round(eager_ms, 5),
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": "paged_attention_kernel",
+                     "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": dec_b,
+                     "kernel_source_hash": src_hash},
+    }
+    if not args.no_secondary:
+        line["secondary"] = secondary(args)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(copies[0], layout, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

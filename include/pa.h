@@ -1,0 +1,158 @@
+/*
+ * pa.h -- paged attention over a block-table KV cache, for AMD MI355X (gfx950).
+ *
+ * The operations follow the problem statement of three web pages, cited by a
+ * short tag and section:
+ *   [P1] "从 token 调度到采样输出，追踪每一步张量维度的变化，搞懂 LLM 推理到底在算什么"
+ *        (zizhi168.cn/news/2384056): 02 Paged Attention, 03 Embedding,
+ *        04 Attention (six steps, GQA mapping, cu_seqlens, Prefill/Decode
+ *        table), 07 extensions (chunked prefill, Flash-Decoding, LSE).
+ *   [P2] "别只当API调用侠了！一文带你深入大模型“体内”，看懂推理全流程"
+ *        (su666666.com/news/35626): PagedAttention deep dive -- paging, the
+ *        block table, copy-on-write sharing, where the block table lives.
+ *   [P3] the LLM inference-optimisation survey at adg.csdn.net
+ *        (695256bb5b9f5f31781b99f3): 1.4 KV cache, 1.5 memory, 3.3 GQA,
+ *        3.4 FlashAttention, 3.5 PageAttention.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is DEVICE memory owned by the caller. The library
+ *   allocates nothing, never synchronises, keeps no mutable global state and
+ *   may be called from several host threads at once.
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL means the null stream). Results are ready when the stream is.
+ * - Tensors are dense and row-major with exactly the shapes written in the
+ *   comments (no strides). B = num_seqs, T = num_tokens, Hq = num_heads,
+ *   Hkv = num_kv_heads, D = head_dim, bs = block_size.
+ * - Host-side validation returns a pa_status and launches nothing on error;
+ *   nothing prints or aborts. A failed launch returns PA_ERR_LAUNCH.
+ * - Device-resident metadata (slot_mapping, block_table, seq_lens,
+ *   cu_seqlens_q) is the caller's contract, as it is the CPU scheduler's in
+ *   [P2 "深度解析块表究竟存在哪里"]: slots lie inside the pool, slot_mapping
+ *   has no duplicate (two writes to one slot would race), every request has a
+ *   table entry for each of its blocks, seq_len >= query_len, and the host
+ *   hints max_seq_len / max_query_len bound every request. The kernels never
+ *   read or write outside the buffers described here even when the contract
+ *   is broken: an out-of-pool slot is not written, an out-of-pool block id is
+ *   read as an empty block, lengths are clipped to max_blocks_per_seq * bs.
+ *   Results for such inputs are unspecified.
+ * - Supported now: block_size 16; head_dim 64 or 128; Hq % Hkv == 0 with
+ *   Hq / Hkv <= 16; fp32, fp16 and bf16 storage with fp32 accumulation.
+ *   Anything else returns PA_ERR_UNSUPPORTED.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,       /* inconsistent or negative sizes */
+  PA_ERR_DTYPE = -3,       /* unknown dtype */
+  PA_ERR_UNSUPPORTED = -4, /* valid but not implemented (see above) */
+  PA_ERR_WORKSPACE = -5,   /* split-K workspace arguments inconsistent */
+  PA_ERR_LAUNCH = -6       /* the HIP runtime rejected a kernel launch */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* One layer's paged KV cache [P1 §02]: the pages' pool
+ * [num_layers, 2, num_blocks, block_size, num_kv_heads, head_dim] seen for one
+ * layer as two tensors, K and V, each [num_blocks, block_size, Hkv, D] in
+ * `dtype`. Slot s is row s % bs of physical block s / bs, a contiguous run of
+ * Hkv * D elements. */
+typedef struct {
+  void *k_cache;
+  void *v_cache;
+  int num_blocks;
+  int block_size;
+  int num_kv_heads;
+  int head_dim;
+  pa_dtype dtype;
+} pa_kv_cache;
+
+/* KV write [P1 §02; P3 §1.4]: for each token i with s = slot_mapping[i] >= 0,
+ * copy k_new[i] to K slot s and v_new[i] to V slot s, bit for bit.
+ *   k_new, v_new : [T, Hkv, D] in cache->dtype
+ *   slot_mapping : int64 [T]; a negative entry means "do not write"
+ * T == 0 is a no-op. */
+pa_status pa_write_kv(const pa_kv_cache *cache, const void *k_new, const void *v_new,
+                      const int64_t *slot_mapping, int num_tokens, void *stream);
+
+/* Paged decode attention [P1 §04; P2 paging; P3 §3.3-3.5]: one query row per
+ * request against all of its KV, gathered through the block table. Query
+ * head h reads KV head h / (Hq / Hkv) [P1 §04]. The new token is part of the
+ * KV (write it with pa_write_kv first, on the same stream).
+ *   out          : [B, Hq, D] in cache->dtype; out = softmax(scale q K^T) V
+ *   q            : [B, Hq, D] in cache->dtype
+ *   block_table  : int32 [B, max_blocks_per_seq]; entry j of row r is the
+ *                  physical block holding tokens [16j, 16j+16) of request r
+ *   seq_lens     : int32 [B]; KV length of each request, this token included
+ *   max_seq_len  : host upper bound on seq_lens (sizes the launch)
+ * A request with seq_len 0 gets out = 0. */
+pa_status pa_decode(const pa_kv_cache *cache, void *out, const void *q,
+                    const int32_t *block_table, const int32_t *seq_lens, int num_seqs,
+                    int num_heads, int max_blocks_per_seq, int max_seq_len, float scale,
+                    void *stream);
+
+/* Number of KV splits S used by the split-K pair below: ceil(max_seq_len /
+ * split_tokens), at least 1. Returns 0 if split_tokens <= 0. */
+int pa_splitk_num_splits(int max_seq_len, int split_tokens);
+
+/* Split-K (Flash-Decoding) partials [P1 §07]: split j of request r covers
+ * tokens [j*split_tokens, min((j+1)*split_tokens, seq_len)).
+ *   o_part   : fp32 [B, Hq, S, D]; split j's softmax-normalised output
+ *   lse_part : fp32 [B, Hq, S]; split j's natural-log log-sum-exp of the
+ *              scaled scores; -inf (with o_part 0) for an empty split
+ *   S        = pa_splitk_num_splits(max_seq_len, split_tokens)
+ *   split_tokens must be a positive multiple of block_size.
+ * Other arguments as for pa_decode. */
+pa_status pa_decode_splitk(const pa_kv_cache *cache, float *o_part, float *lse_part,
+                           const void *q, const int32_t *block_table,
+                           const int32_t *seq_lens, int num_seqs, int num_heads,
+                           int max_blocks_per_seq, int max_seq_len, int split_tokens,
+                           float scale, void *stream);
+
+/* Log-sum-exp merge of split-K partials [P1 §07]: with M = max_j lse_j and
+ * w_j = exp(lse_j - M), out = sum_j w_j o_j / sum_j w_j and
+ * lse = M + log(sum_j w_j), over the ceil(seq_len / split_tokens) splits of
+ * each request. A request with seq_len 0 gets out = 0, lse = -inf.
+ *   out     : [B, Hq, D] in out_dtype
+ *   lse_out : fp32 [B, Hq], or NULL
+ *   o_part, lse_part : as written by pa_decode_splitk with the same
+ *             (max_seq_len, split_tokens). */
+pa_status pa_lse_merge(void *out, float *lse_out, const float *o_part,
+                       const float *lse_part, const int32_t *seq_lens, int num_seqs,
+                       int num_heads, int head_dim, int max_seq_len, int split_tokens,
+                       pa_dtype out_dtype, void *stream);
+
+/* Varlen mixed step [P1 §03/§04 flattened batch and cu_seqlens; P1 §07
+ * chunked prefill]: request r owns query rows [cu[r], cu[r+1]) of the
+ * flattened batch; n_r = cu[r+1] - cu[r] and its earlier context is
+ * c_r = seq_len[r] - n_r. With causal != 0, row i of the request sees keys
+ * 0 .. c_r + i (a query sees itself and earlier tokens); with causal == 0,
+ * all seq_len[r] keys. Decode rows are the n_r == 1 case.
+ *   out, q        : [T, Hq, D] in cache->dtype
+ *   cu_seqlens_q  : int32 [B + 1], cu[0] = 0, non-decreasing, cu[B] = T
+ *   seq_lens      : int32 [B]; KV length including this step's n_r tokens
+ *   max_query_len, max_seq_len : host upper bounds (size the launch) */
+pa_status pa_varlen(const pa_kv_cache *cache, void *out, const void *q,
+                    const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                    const int32_t *block_table, int num_seqs, int num_tokens,
+                    int num_heads, int max_blocks_per_seq, int max_query_len,
+                    int max_seq_len, float scale, int causal, void *stream);
+
+/* Static English text for a status code. */
+const char *pa_status_str(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

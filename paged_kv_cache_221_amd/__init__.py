@@ -1,0 +1,19 @@
+"""Paged attention over a block-table KV cache for AMD MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+``include/pa.h`` (``libpa.so``, built in-tree by ``build.build()``); this
+package only marshals torch tensors into those calls.
+"""
+
+from ._native import load  # noqa: F401
+from .api import (  # noqa: F401
+    PaError,
+    kv_cache_struct,
+    pa_decode,
+    pa_decode_splitk,
+    pa_lse_merge,
+    pa_splitk_num_splits,
+    pa_status_str,
+    pa_varlen,
+    pa_write_kv,
+)

@@ -1,0 +1,71 @@
+"""ctypes declarations of the C ABI in ``include/pa.h``.
+
+Loads ``libpa.so`` from this package directory. There is no fallback: if the
+library is missing, every entry point raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "pa.h")
+
+PA_OK = 0
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+class PaKvCache(ctypes.Structure):
+    _fields_ = [
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int),
+        ("block_size", ctypes.c_int),
+        ("num_kv_heads", ctypes.c_int),
+        ("head_dim", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+    ]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_CACHE = ctypes.POINTER(PaKvCache)
+
+SIGNATURES = {
+    "pa_write_kv": (_I, [_CACHE, _P, _P, _P, _I, _P]),
+    "pa_decode": (_I, [_CACHE, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
+    "pa_splitk_num_splits": (_I, [_I, _I]),
+    "pa_decode_splitk": (_I, [_CACHE, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "pa_lse_merge": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "pa_varlen": (_I, [_CACHE, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "pa_status_str": (ctypes.c_char_p, [_I]),
+}
+
+_lib = None
+
+
+def header_symbols() -> list[str]:
+    """Names of the functions ``include/pa.h`` declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc for gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

@@ -1,0 +1,188 @@
+"""Python binding of the C ABI: same names, argument marshalling only.
+
+Each function checks that the torch tensors it is handed are contiguous GPU
+tensors with the dtypes and shapes ``include/pa.h`` requires, passes their
+device pointers and torch's current stream to ``libpa.so``, and raises
+``PaError`` on a non-OK status. Output tensors are allocated with torch when
+the caller does not pass them. No step of the computation happens here, and
+there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _native
+
+_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+class PaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = _native.load()
+        super().__init__(f"{fn}: {lib.pa_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != _native.PA_OK:
+        raise PaError(fn, status)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    return t
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def kv_cache_struct(k_cache: torch.Tensor, v_cache: torch.Tensor) -> _native.PaKvCache:
+    """``pa_kv_cache`` for one layer's K and V pools ``[num_blocks, bs, Hkv, D]``."""
+    _dev(k_cache, "k_cache")
+    _dev(v_cache, "v_cache", k_cache.dtype)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [num_blocks, block_size, Hkv, D]")
+    if k_cache.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
+    if k_cache.device != v_cache.device:
+        raise ValueError("k_cache and v_cache must be on one device")
+    nb, bs, hkv, d = k_cache.shape
+    return _native.PaKvCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, d,
+                             _DTYPE_CODE[k_cache.dtype])
+
+
+def pa_status_str(status: int) -> str:
+    return _native.load().pa_status_str(status).decode()
+
+
+def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping) -> None:
+    lib = _native.load()
+    c = kv_cache_struct(k_cache, v_cache)
+    t = slot_mapping.shape[0]
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        _dev(x, name, k_cache.dtype)
+        if tuple(x.shape) != (t, c.num_kv_heads, c.head_dim):
+            raise ValueError(f"{name} must be [num_tokens, Hkv, D]")
+    _check("pa_write_kv", lib.pa_write_kv(ctypes.byref(c), _ptr(k_new), _ptr(v_new),
+                                          _ptr(slot_mapping), t, _stream(k_cache)))
+
+
+def _attention_meta(c, block_table, seq_lens, num_seqs):
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != num_seqs:
+        raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
+    if tuple(seq_lens.shape) != (num_seqs,):
+        raise ValueError("seq_lens must be [num_seqs]")
+    return block_table.shape[1]
+
+
+def pa_decode(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int, scale: float,
+              out=None):
+    lib = _native.load()
+    c = kv_cache_struct(k_cache, v_cache)
+    _dev(q, "q", k_cache.dtype)
+    if q.dim() != 3 or q.shape[2] != c.head_dim:
+        raise ValueError("q must be [num_seqs, Hq, D]")
+    b, hq, _ = q.shape
+    max_blocks = _attention_meta(c, block_table, seq_lens, b)
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check("pa_decode", lib.pa_decode(ctypes.byref(c), _ptr(out), _ptr(q), _ptr(block_table),
+                                      _ptr(seq_lens), b, hq, max_blocks, int(max_seq_len),
+                                      float(scale), _stream(q)))
+    return out
+
+
+def pa_splitk_num_splits(max_seq_len: int, split_tokens: int) -> int:
+    return int(_native.load().pa_splitk_num_splits(int(max_seq_len), int(split_tokens)))
+
+
+def pa_decode_splitk(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int,
+                     split_tokens: int, scale: float, o_part=None, lse_part=None):
+    lib = _native.load()
+    c = kv_cache_struct(k_cache, v_cache)
+    _dev(q, "q", k_cache.dtype)
+    if q.dim() != 3 or q.shape[2] != c.head_dim:
+        raise ValueError("q must be [num_seqs, Hq, D]")
+    b, hq, d = q.shape
+    max_blocks = _attention_meta(c, block_table, seq_lens, b)
+    s = pa_splitk_num_splits(max_seq_len, split_tokens)
+    if o_part is None:
+        o_part = torch.empty((b, hq, max(s, 1), d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((b, hq, max(s, 1)), dtype=torch.float32, device=q.device)
+    _dev(o_part, "o_part", torch.float32)
+    _dev(lse_part, "lse_part", torch.float32)
+    if s > 0 and (tuple(o_part.shape) != (b, hq, s, d) or tuple(lse_part.shape) != (b, hq, s)):
+        raise ValueError(f"o_part/lse_part must be [B, Hq, {s}, D] / [B, Hq, {s}]")
+    _check("pa_decode_splitk", lib.pa_decode_splitk(
+        ctypes.byref(c), _ptr(o_part), _ptr(lse_part), _ptr(q), _ptr(block_table),
+        _ptr(seq_lens), b, hq, max_blocks, int(max_seq_len), int(split_tokens), float(scale),
+        _stream(q)))
+    return o_part, lse_part
+
+
+def pa_lse_merge(o_part, lse_part, seq_lens, max_seq_len: int, split_tokens: int,
+                 out_dtype=torch.float32, out=None, lse_out=None, want_lse: bool = False):
+    lib = _native.load()
+    _dev(o_part, "o_part", torch.float32)
+    _dev(lse_part, "lse_part", torch.float32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    b, hq, s, d = o_part.shape
+    if tuple(lse_part.shape) != (b, hq, s) or tuple(seq_lens.shape) != (b,):
+        raise ValueError("inconsistent o_part / lse_part / seq_lens shapes")
+    if s != pa_splitk_num_splits(max_seq_len, split_tokens):
+        raise ValueError("o_part's split count does not match max_seq_len / split_tokens")
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported out dtype {out_dtype}")
+    out = torch.empty((b, hq, d), dtype=out_dtype, device=o_part.device) if out is None \
+        else _dev(out, "out", out_dtype)
+    if lse_out is None and want_lse:
+        lse_out = torch.empty((b, hq), dtype=torch.float32, device=o_part.device)
+    if lse_out is not None:
+        _dev(lse_out, "lse_out", torch.float32)
+    _check("pa_lse_merge", lib.pa_lse_merge(
+        _ptr(out), _ptr(lse_out), _ptr(o_part), _ptr(lse_part), _ptr(seq_lens), b, hq, d,
+        int(max_seq_len), int(split_tokens), _DTYPE_CODE[out_dtype], _stream(o_part)))
+    return (out, lse_out) if lse_out is not None else out
+
+
+def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_query_len: int,
+              max_seq_len: int, scale: float, causal: bool = True, out=None):
+    lib = _native.load()
+    c = kv_cache_struct(k_cache, v_cache)
+    _dev(q, "q", k_cache.dtype)
+    if q.dim() != 3 or q.shape[2] != c.head_dim:
+        raise ValueError("q must be [num_tokens, Hq, D]")
+    t, hq, _ = q.shape
+    b = seq_lens.shape[0]
+    max_blocks = _attention_meta(c, block_table, seq_lens, b)
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    if tuple(cu_seqlens_q.shape) != (b + 1,):
+        raise ValueError("cu_seqlens_q must be [num_seqs + 1]")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check("pa_varlen", lib.pa_varlen(
+        ctypes.byref(c), _ptr(out), _ptr(q), _ptr(cu_seqlens_q), _ptr(seq_lens),
+        _ptr(block_table), b, t, hq, max_blocks, int(max_query_len), int(max_seq_len),
+        float(scale), 1 if causal else 0, _stream(q)))
+    return out

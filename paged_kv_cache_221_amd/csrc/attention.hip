@@ -1,0 +1,242 @@
+// attention.hip -- paged attention kernel for decode, split-K partials and
+// varlen mixed steps on gfx950.
+//
+// One workgroup works on one (query tile, request, KV head, KV split).
+// - A request whose query rows times the GQA group fit one 16-row tile
+//   (decode, [P1 §04 table]: query_len 1; also short multi-token queries)
+//   is a "single-tile" unit: the waves of the workgroup take interleaved KV
+//   blocks of the split and their partial softmax states are merged through
+//   LDS at the end. Decode streams the whole KV from HBM, so this is the
+//   bandwidth-bound path ([P1 §04], [P3 §1.2]).
+// - A longer query (chunked prefill, [P1 §07]) is cut into tiles; each wave
+//   owns 16 rows (tokens x heads of one KV group) and streams every KV block
+//   its rows can see under the causal mask.
+// Split-K (Flash-Decoding, [P1 §07]) writes each split's normalised output
+// and its natural-log LSE; pa_lse_merge renormalises them.
+#include "attn_tile.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+template <class E, int D>
+__device__ inline void store_chunk(typename Ops<E, D>::storage* dst, const float* v) {
+  constexpr int n = D / 16;
+  using S = typename Ops<E, D>::storage;
+  if constexpr (sizeof(S) == 2) {
+    unsigned w[n / 2];
+#pragma unroll
+    for (int j = 0; j < n / 2; ++j)
+      w[j] = (unsigned)Ops<E, D>::to_storage(v[2 * j]) |
+             ((unsigned)Ops<E, D>::to_storage(v[2 * j + 1]) << 16);
+    if constexpr (n == 8) {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < n / 4; ++j)
+      *reinterpret_cast<f32x4*>(dst + 4 * j) = f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2],
+                                                    v[4 * j + 3]};
+  }
+}
+
+template <class E, int D, int NW>
+__global__ __launch_bounds__(NW * kWave) void paged_attention_kernel(const AttnArgs a) {
+  using O = Ops<E, D>;
+  using S = typename O::storage;
+  constexpr int kComb = NW > 1 ? NW : 1;
+  __shared__ float sm_o[kComb][16][NW > 1 ? D : 1];
+  __shared__ float sm_m[kComb][16];
+  __shared__ float sm_l[kComb][16];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  int u = blockIdx.x;
+  const int split = u % a.num_splits;
+  u /= a.num_splits;
+  const int kvh = u % a.num_kv_heads;
+  u /= a.num_kv_heads;
+  const int r = u % a.num_seqs;
+  const int tile = u / a.num_seqs;
+
+  int q_lo = r, n = 1;
+  if (a.cu_seqlens != nullptr) {
+    int lo = a.cu_seqlens[r], hi = a.cu_seqlens[r + 1];
+    lo = min(max(lo, 0), a.num_tokens);
+    hi = min(max(hi, lo), a.num_tokens);
+    q_lo = lo;
+    n = hi - lo;
+  }
+  int seq_len = a.seq_lens[r];
+  seq_len = min(max(seq_len, 0), a.max_blocks * kBlockTokens);
+  const int g = a.group;
+  const int ctx = max(seq_len - n, 0);
+  const int row = lane & 15;
+  const int grp = lane >> 4;
+
+  KvView<S> view;
+  view.k = static_cast<const S*>(a.k_cache) + (int64_t)kvh * D;
+  view.v = static_cast<const S*>(a.v_cache) + (int64_t)kvh * D;
+  view.rs = (int64_t)a.num_kv_heads * D;
+  view.table = a.block_table + (int64_t)r * a.max_blocks;
+  view.num_blocks = a.num_blocks;
+
+  typename O::Q qop;
+  RowState<D> st;
+  st.init();
+
+  if (n * g <= 16) {
+    // ---------------------------------------------------- single-tile unit
+    if (tile != 0 || n == 0) return;
+    const int tok = row / g, hh = row - (row / g) * g;
+    const bool valid = row < n * g;
+    const int key_end = !valid ? 0 : (a.causal ? min(ctx + tok + 1, seq_len) : seq_len);
+    const S* qrow = static_cast<const S*>(a.q) +
+                    ((int64_t)(q_lo + (valid ? tok : 0)) * a.num_heads + kvh * g + hh) * D;
+    O::load_q(qop, qrow, valid, lane);
+    const int nblk = (seq_len + kBlockTokens - 1) / kBlockTokens;
+    const int b0 = split * a.split_blocks;
+    const int b1 = min(b0 + a.split_blocks, nblk);
+    stream_blocks<E, D>(st, qop, view, b0 + wave, b1, NW, key_end, seq_len, a.scale_log2,
+                        lane);
+    st.l += xor_shuffle(st.l, 16);
+    st.l += xor_shuffle(st.l, 32);
+
+    const int nrows = n * g;
+    auto emit = [&](int rr, int d, float acc, float lsum, float mx) {
+      const int head = kvh * g + rr % g;
+      const float val = lsum > 0.f ? acc / lsum : 0.f;
+      if (a.o_part != nullptr) {
+        const int64_t unit = (int64_t)r * a.num_heads + head;
+        a.o_part[(unit * a.num_splits + split) * D + d] = val;
+        if (d == 0)
+          a.lse_part[unit * a.num_splits + split] =
+              lsum > 0.f ? (mx + fast_log2(lsum)) * kLn2 : neg_inf();
+      } else {
+        S* dst = static_cast<S*>(a.out) + ((int64_t)(q_lo + rr / g) * a.num_heads + head) * D;
+        dst[d] = O::to_storage(val);
+      }
+    };
+
+    if constexpr (NW > 1) {
+      if (lane < 16) {
+        sm_m[wave][lane] = st.m;
+        sm_l[wave][lane] = st.l;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) sm_o[wave][row][(D / 4) * grp + (D / 16) * i + c] = st.o[c][i];
+      __syncthreads();
+      for (int it = threadIdx.x; it < nrows * D; it += NW * kWave) {
+        const int rr = it / D, d = it - (it / D) * D;
+        float mx = neg_inf();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][rr]);
+        const float mu = mx == neg_inf() ? 0.f : mx;
+        float lsum = 0.f, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float e = fast_exp2(sm_m[w][rr] - mu);
+          lsum += e * sm_l[w][rr];
+          acc += e * sm_o[w][rr][d];
+        }
+        emit(rr, d, acc, lsum, mx);
+      }
+    } else {
+      if (row < nrows) {
+        if (a.o_part == nullptr) {
+          const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+          S* dst = static_cast<S*>(a.out) +
+                   ((int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh) * D + (D / 4) * grp;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v[D / 16];
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) v[c] = st.o[c][i] * inv;
+            store_chunk<E, D>(dst + (D / 16) * i, v);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c)
+              emit(row, (D / 4) * grp + (D / 16) * i + c, st.o[c][i], st.l, st.m);
+        }
+      }
+    }
+    return;
+  }
+
+  // ----------------------------------------------------------- tiled prefill
+  const int tpw = 16 / g;  // query tokens per wave
+  const int tok0 = (tile * NW + wave) * tpw;
+  if (tok0 >= n) return;
+  const int tok = tok0 + row / g, hh = row - (row / g) * g;
+  const bool valid = row < tpw * g && tok < n;
+  const int key_end = !valid ? 0 : (a.causal ? min(ctx + tok + 1, seq_len) : seq_len);
+  const S* qrow = static_cast<const S*>(a.q) +
+                  ((int64_t)(q_lo + (valid ? tok : 0)) * a.num_heads + kvh * g + hh) * D;
+  O::load_q(qop, qrow, valid, lane);
+  const int last = min(tok0 + tpw, n) - 1;
+  const int kmax = a.causal ? min(ctx + last + 1, seq_len) : seq_len;
+  stream_blocks<E, D>(st, qop, view, 0, (kmax + kBlockTokens - 1) / kBlockTokens, 1, key_end,
+                      seq_len, a.scale_log2, lane);
+  st.l += xor_shuffle(st.l, 16);
+  st.l += xor_shuffle(st.l, 32);
+  if (valid) {
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    S* dst = static_cast<S*>(a.out) + ((int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh) * D +
+             (D / 4) * grp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[D / 16];
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) v[c] = st.o[c][i] * inv;
+      store_chunk<E, D>(dst + (D / 16) * i, v);
+    }
+  }
+}
+
+template <class E, int D>
+hipError_t launch_dw(const AttnArgs& a, int waves, int64_t grid, hipStream_t stream) {
+  switch (waves) {
+    case 1:
+      paged_attention_kernel<E, D, 1><<<dim3((unsigned)grid), dim3(kWave), 0, stream>>>(a);
+      break;
+    case 2:
+      paged_attention_kernel<E, D, 2><<<dim3((unsigned)grid), dim3(2 * kWave), 0, stream>>>(a);
+      break;
+    case 4:
+      paged_attention_kernel<E, D, 4><<<dim3((unsigned)grid), dim3(4 * kWave), 0, stream>>>(a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_d(const AttnArgs& a, int head_dim, int waves, int64_t grid,
+                    hipStream_t stream) {
+  if (head_dim == 128) return launch_dw<E, 128>(a, waves, grid, stream);
+  if (head_dim == 64) return launch_dw<E, 64>(a, waves, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& args, pa_dtype dtype, int head_dim, int waves,
+                            int64_t grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  switch (dtype) {
+    case PA_BF16: return launch_d<Bf16>(args, head_dim, waves, grid, stream);
+    case PA_F16: return launch_d<F16>(args, head_dim, waves, grid, stream);
+    case PA_F32: return launch_d<F32>(args, head_dim, waves, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

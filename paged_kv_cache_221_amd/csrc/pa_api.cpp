@@ -1,0 +1,213 @@
+// pa_api.cpp -- the C ABI of include/pa.h: host-side validation, launch
+// sizing from host-known sizes and hints, and dispatch. Nothing here reads
+// device memory or synchronises.
+#include <math.h>
+
+#include "pa_launch.h"
+
+namespace {
+
+using pa::AttnArgs;
+
+constexpr int kSupportedBlock = 16;
+constexpr int kMaxGroup = 16;
+
+bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+
+pa_status check_cache(const pa_kv_cache* c) {
+  if (c == nullptr || c->k_cache == nullptr || c->v_cache == nullptr) return PA_ERR_NULL;
+  if (!dtype_ok(c->dtype)) return PA_ERR_DTYPE;
+  if (c->num_blocks <= 0 || c->block_size <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
+    return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+pa_status check_attention_shape(const pa_kv_cache* c, int num_seqs, int num_heads,
+                                int max_blocks_per_seq, int max_seq_len, float scale) {
+  if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_heads % c->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * c->block_size) return PA_ERR_SHAPE;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (c->block_size != kSupportedBlock) return PA_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_heads / c->num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+pa_status launched(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+AttnArgs base_args(const pa_kv_cache* c, const void* q, const int32_t* block_table,
+                   const int32_t* seq_lens, int num_seqs, int num_heads,
+                   int max_blocks_per_seq, float scale) {
+  AttnArgs a{};
+  a.k_cache = c->k_cache;
+  a.v_cache = c->v_cache;
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = c->num_kv_heads;
+  a.group = num_heads / c->num_kv_heads;
+  a.num_blocks = c->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_splits = 1;
+  a.num_tiles = 1;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.causal = 1;
+  return a;
+}
+
+// Waves per workgroup for a single-tile (decode-like) unit covering
+// `blocks` KV blocks: more waves give a long split more loads in flight.
+int decode_waves(int blocks) {
+  if (blocks >= 64) return 4;
+  if (blocks >= 16) return 2;
+  return 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "inconsistent or invalid sizes";
+    case PA_ERR_DTYPE: return "unknown dtype";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "split-K workspace arguments are inconsistent";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+pa_status pa_write_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping, int num_tokens, void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
+  const int elem = cache->dtype == PA_F32 ? 4 : 2;
+  if (((int64_t)cache->num_kv_heads * cache->head_dim * elem) % 16 != 0)
+    return PA_ERR_UNSUPPORTED;
+  return launched(pa::launch_write_kv(cache, k_new, v_new, slot_mapping, num_tokens,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* q,
+                    const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
+                    int num_heads, int max_blocks_per_seq, int max_seq_len, float scale,
+                    void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  s = check_attention_shape(cache, num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale);
+  if (s != PA_OK) return s;
+  if (num_seqs == 0) return PA_OK;
+  if (out == nullptr || q == nullptr || block_table == nullptr || seq_lens == nullptr)
+    return PA_ERR_NULL;
+  AttnArgs a = base_args(cache, q, block_table, seq_lens, num_seqs, num_heads,
+                         max_blocks_per_seq, scale);
+  a.out = out;
+  a.num_tokens = num_seqs;
+  const int max_blocks = (max_seq_len + kSupportedBlock - 1) / kSupportedBlock;
+  a.split_blocks = max_blocks_per_seq;
+  const int64_t grid = (int64_t)num_seqs * cache->num_kv_heads;
+  return launched(pa::launch_attention(a, cache->dtype, cache->head_dim,
+                                       decode_waves(max_blocks), grid,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int pa_splitk_num_splits(int max_seq_len, int split_tokens) {
+  if (split_tokens <= 0) return 0;
+  const int s = (max_seq_len + split_tokens - 1) / split_tokens;
+  return s > 0 ? s : 1;
+}
+
+pa_status pa_decode_splitk(const pa_kv_cache* cache, float* o_part, float* lse_part,
+                           const void* q, const int32_t* block_table, const int32_t* seq_lens,
+                           int num_seqs, int num_heads, int max_blocks_per_seq, int max_seq_len,
+                           int split_tokens, float scale, void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  s = check_attention_shape(cache, num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale);
+  if (s != PA_OK) return s;
+  if (split_tokens <= 0 || split_tokens % cache->block_size != 0) return PA_ERR_WORKSPACE;
+  if (num_seqs == 0) return PA_OK;
+  if (o_part == nullptr || lse_part == nullptr || q == nullptr || block_table == nullptr ||
+      seq_lens == nullptr)
+    return PA_ERR_NULL;
+  AttnArgs a = base_args(cache, q, block_table, seq_lens, num_seqs, num_heads,
+                         max_blocks_per_seq, scale);
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.num_tokens = num_seqs;
+  a.num_splits = pa_splitk_num_splits(max_seq_len, split_tokens);
+  a.split_blocks = split_tokens / cache->block_size;
+  const int64_t grid = (int64_t)num_seqs * cache->num_kv_heads * a.num_splits;
+  if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  return launched(pa::launch_attention(a, cache->dtype, cache->head_dim,
+                                       decode_waves(a.split_blocks), grid,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_lse_merge(void* out, float* lse_out, const float* o_part, const float* lse_part,
+                       const int32_t* seq_lens, int num_seqs, int num_heads, int head_dim,
+                       int max_seq_len, int split_tokens, pa_dtype out_dtype, void* stream) {
+  if (!dtype_ok(out_dtype)) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len < 0) return PA_ERR_SHAPE;
+  if (split_tokens <= 0) return PA_ERR_WORKSPACE;
+  if (num_seqs == 0) return PA_OK;
+  if (out == nullptr || o_part == nullptr || lse_part == nullptr || seq_lens == nullptr)
+    return PA_ERR_NULL;
+  pa::MergeArgs a{};
+  a.out = out;
+  a.lse_out = lse_out;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.num_splits = pa_splitk_num_splits(max_seq_len, split_tokens);
+  a.split_tokens = split_tokens;
+  return launched(pa::launch_lse_merge(a, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
+                    const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                    const int32_t* block_table, int num_seqs, int num_tokens, int num_heads,
+                    int max_blocks_per_seq, int max_query_len, int max_seq_len, float scale,
+                    int causal, void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  s = check_attention_shape(cache, num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale);
+  if (s != PA_OK) return s;
+  if (num_tokens < 0 || max_query_len < 0 || max_query_len > max_seq_len) return PA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (out == nullptr || q == nullptr || cu_seqlens_q == nullptr || seq_lens == nullptr ||
+      block_table == nullptr)
+    return PA_ERR_NULL;
+  AttnArgs a = base_args(cache, q, block_table, seq_lens, num_seqs, num_heads,
+                         max_blocks_per_seq, scale);
+  a.out = out;
+  a.cu_seqlens = cu_seqlens_q;
+  a.num_tokens = num_tokens;
+  a.causal = causal;
+  a.split_blocks = max_blocks_per_seq;
+  const int waves = 4;
+  const int tokens_per_tile = waves * (16 / a.group);
+  a.num_tiles = max_query_len * a.group <= 16
+                    ? 1
+                    : (max_query_len + tokens_per_tile - 1) / tokens_per_tile;
+  const int64_t grid = (int64_t)a.num_tiles * num_seqs * cache->num_kv_heads;
+  if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  return launched(pa::launch_attention(a, cache->dtype, cache->head_dim, waves, grid,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

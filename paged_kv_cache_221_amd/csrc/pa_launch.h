@@ -1,0 +1,58 @@
+// pa_launch.h -- internal launch interface between the C API and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+// Arguments of the paged attention kernel (decode, split-K partials, varlen).
+struct AttnArgs {
+  const void* k_cache;
+  const void* v_cache;
+  const void* q;             // [T or B, Hq, D]
+  void* out;                 // final output, or nullptr when writing partials
+  float* o_part;             // [B, Hq, S, D] split partials, or nullptr
+  float* lse_part;           // [B, Hq, S]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens;  // nullptr: one query row per request (row r)
+  int num_seqs;
+  int num_tokens;
+  int num_heads;
+  int num_kv_heads;
+  int group;                 // num_heads / num_kv_heads
+  int num_blocks;
+  int max_blocks;            // block_table row length
+  int num_splits;            // S (1 unless writing partials)
+  int split_blocks;          // KV blocks per split
+  int num_tiles;             // query tiles per request (varlen)
+  float scale_log2;          // scale * log2(e)
+  int causal;
+};
+
+struct MergeArgs {
+  void* out;
+  float* lse_out;
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* seq_lens;
+  int num_seqs;
+  int num_heads;
+  int head_dim;
+  int num_splits;
+  int split_tokens;
+};
+
+// Waves per workgroup the attention kernel is built for.
+constexpr int kAttnWaves[] = {1, 2, 4};
+
+hipError_t launch_write_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, int num_tokens, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs& args, pa_dtype dtype, int head_dim, int waves,
+                            int64_t grid, hipStream_t stream);
+hipError_t launch_lse_merge(const MergeArgs& args, pa_dtype out_dtype, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,151 @@
+"""GPU parity at the five workloads' full sizes.
+
+Every cache write is checked bit for bit on the blocks the sampled requests
+and the new tokens touch, and the rest of the pool is checked unchanged on the
+GPU against a copy taken before the write. Attention outputs are compared
+with the fp64 oracle for every request where that takes seconds, otherwise for
+a seeded sample that includes the longest requests, the prefill chunks and
+requests sharing the copy-on-write prefix.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_221_amd as pa
+from workloads import (llama2_7b_mha_decode, llama3_8b_decode, long_context_splitk,
+                       mixed_step, tiny_decode_fp32)
+from workloads.tensors import materialize
+
+from _parity import (TOL, Snapshot, check_cache_after_write, gpu_rows, gpu_write, max_err,
+                     rows_of)
+
+pytestmark = pytest.mark.gpu
+
+BENCH_SPLIT_TOKENS = 512
+
+
+def _write_and_check(st, requests):
+    lay = st.layout
+    full = lay.num_blocks * lay.block_size * lay.num_kv_heads * lay.head_dim <= (1 << 24)
+    snap = Snapshot(st, requests, full)
+    k_before, v_before = st.k_cache.clone(), st.v_cache.clone()
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    torch.cuda.synchronize()
+    check_cache_after_write(st, snap)
+    # every slot outside slot_mapping is bitwise unchanged
+    nslots = lay.num_blocks * lay.block_size
+    keep = torch.ones(nslots, dtype=torch.bool, device=st.k_cache.device)
+    keep[st.slot_mapping[st.slot_mapping >= 0]] = False
+    raw = torch.int32 if lay.dtype == "f32" else torch.int16
+    for after, before in ((st.k_cache, k_before), (st.v_cache, v_before)):
+        a = after.view(raw).view(nslots, -1)[keep]
+        b = before.view(raw).view(nslots, -1)[keep]
+        assert torch.equal(a, b), "the write touched a slot outside slot_mapping"
+    del k_before, v_before
+    return snap
+
+
+def _sample(lay, n, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    longest = int(np.argmax(lay.seq_lens))
+    pick = set(rng.choice(lay.num_seqs, size=min(n, lay.num_seqs), replace=False).tolist())
+    pick.add(longest)
+    return sorted(pick)
+
+
+def _decode_check(st, snap, requests, out):
+    lay = st.layout
+    want, _ = oracle.paged_decode(snap.q, snap.k, snap.v, lay.block_table, lay.seq_lens,
+                                  lay.scale, lay.block_size, lay.dtype, requests=requests)
+    got = gpu_rows(out, lay.dtype)
+    err = max_err(got[requests], want[requests])
+    print(f"{lay.name}: {len(requests)} requests, max|err| = {err:.3e}", flush=True)
+    assert err <= TOL[lay.dtype]
+
+
+def test_tiny_decode_fp32_full():
+    lay = tiny_decode_fp32()
+    st = materialize(lay, "cuda")
+    req = list(range(lay.num_seqs))
+    snap = _write_and_check(st, req)
+    out = pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                       lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    _decode_check(st, snap, req, out)
+
+
+@pytest.mark.parametrize("path", ["splitk", "decode"])
+def test_llama3_8b_decode_full(path):
+    lay = llama3_8b_decode()
+    st = materialize(lay, "cuda")
+    req = list(range(lay.num_seqs))
+    snap = _write_and_check(st, req)
+    if path == "decode":
+        out = pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                           lay.max_seq_len, lay.scale)
+    else:
+        o, l = pa.pa_decode_splitk(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                                   lay.max_seq_len, BENCH_SPLIT_TOKENS, lay.scale)
+        out = pa.pa_lse_merge(o, l, st.seq_lens, lay.max_seq_len, BENCH_SPLIT_TOKENS,
+                              out_dtype=st.q.dtype)
+    torch.cuda.synchronize()
+    _decode_check(st, snap, req, out)
+
+
+def test_long_context_splitk_sampled():
+    lay = long_context_splitk()
+    st = materialize(lay, "cuda")
+    req = [0, 7]                       # 32k and 128k tokens
+    snap = _write_and_check(st, req)
+    o, l = pa.pa_decode_splitk(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                               lay.max_seq_len, lay.split_tokens, lay.scale)
+    out, lse = pa.pa_lse_merge(o, l, st.seq_lens, lay.max_seq_len, lay.split_tokens,
+                               out_dtype=st.q.dtype, want_lse=True)
+    torch.cuda.synchronize()
+    _decode_check(st, snap, req, out)
+    _, want_lse = oracle.paged_decode(snap.q, snap.k, snap.v, lay.block_table, lay.seq_lens,
+                                      lay.scale, lay.block_size, lay.dtype, requests=req)
+    assert max_err(lse.cpu().double().numpy()[req], want_lse[req]) <= TOL["bf16"]
+    # the split count per request is ceil(L / 2048): 344 non-empty splits in all
+    nonempty = torch.isfinite(l).any(dim=1).sum().item()
+    assert nonempty == 344
+
+
+def test_llama2_7b_mha_decode_sampled():
+    lay = llama2_7b_mha_decode()
+    st = materialize(lay, "cuda")
+    req = _sample(lay, 6, 44)
+    snap = _write_and_check(st, req)
+    out = pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                       lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    _decode_check(st, snap, req, out)
+
+
+@pytest.mark.parametrize("shuffled", [False, True])
+def test_mixed_step_sampled(shuffled):
+    lay = mixed_step(shuffled=shuffled)
+    st = materialize(lay, "cuda")
+    prefill = [r for r in range(lay.num_seqs) if lay.query_lens[r] > 1]
+    sharers = [r for r in range(lay.num_seqs)
+               if lay.query_lens[r] == 1 and np.array_equal(lay.block_table[r, :64],
+                                                            lay.shared_blocks)]
+    rng = np.random.Generator(np.random.PCG64(55))
+    others = [r for r in range(lay.num_seqs) if r not in prefill and r not in sharers]
+    req = sorted(set(prefill) | set(sharers[:3]) | set(rng.choice(others, 6, replace=False).tolist())
+                 | {int(np.argmax(lay.seq_lens))})
+    snap = _write_and_check(st, req)
+    out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    want, _ = oracle.paged_varlen(snap.q, snap.k, snap.v, lay.cu_seqlens_q, lay.seq_lens,
+                                  lay.block_table, lay.scale, lay.block_size, lay.dtype,
+                                  requests=req)
+    rows = rows_of(lay, req)
+    err = max_err(gpu_rows(out, lay.dtype)[rows], want[rows])
+    print(f"{lay.name}: {len(req)} requests / {len(rows)} rows, max|err| = {err:.3e}",
+          flush=True)
+    assert err <= TOL[lay.dtype]

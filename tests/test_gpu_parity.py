@@ -1,0 +1,238 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small shapes span several KV blocks and end in ragged tails; every cache write
+is compared bit for bit; attention outputs must be within 2e-2 (fp16/bf16
+storage, fp32 accumulation) or 1e-4 (fp32) of the fp64 oracle, max-abs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_221_amd as pa
+from workloads import small_decode, small_varlen, tiny_decode_fp32
+from workloads.tensors import materialize, raw_bits
+
+from _parity import (TOL, check_cache_after_write, decode_oracle, gpu_rows, gpu_write,
+                     max_err, prepare, rows_of, varlen_oracle)
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_case(layout, waves_hint=None):
+    st, snap, req = prepare(layout)
+    gpu_write(st)
+    snap.apply_oracle_write(layout)
+    check_cache_after_write(st, snap)
+    out = pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                       layout.max_seq_len, layout.scale)
+    torch.cuda.synchronize()
+    want, _ = decode_oracle(st, snap, req)
+    err = max_err(gpu_rows(out, layout.dtype), want)
+    print(f"{layout.name}: decode max|err| = {err:.3e}", flush=True)
+    assert err <= TOL[layout.dtype]
+    return st, out
+
+
+# --------------------------------------------------------------------- write
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_write_kv_bit_exact(gpu_lib, dtype):
+    lay = small_varlen(11, dtype=dtype, head_dim=64)
+    st, snap, _ = prepare(lay, full=True)
+    # a padding token (negative slot) must not write anything
+    st.slot_mapping[3] = -1
+    lay.slot_mapping = lay.slot_mapping.copy()
+    lay.slot_mapping[3] = -1
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    torch.cuda.synchronize()
+    check_cache_after_write(st, snap)
+
+
+def test_write_kv_preserves_nan_payloads_and_signed_zero(gpu_lib):
+    lay = small_decode(12, dtype="bf16", batch=4, head_dim=128)
+    st, snap, _ = prepare(lay, full=True)
+    kn = st.k_new.view(torch.int16)
+    kn[0, 0, 0] = 0x7FC1       # a NaN with a payload
+    kn[1, 1, 5] = -32768       # -0.0 (0x8000)
+    snap.k_new = raw_bits(st.k_new, "bf16")
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    torch.cuda.synchronize()
+    check_cache_after_write(st, snap)
+
+
+# -------------------------------------------------------------------- decode
+DECODE_CASES = [
+    # dtype, head_dim, Hq, Hkv
+    ("bf16", 128, 8, 2), ("bf16", 128, 32, 8), ("bf16", 64, 8, 8), ("bf16", 128, 16, 1),
+    ("f16", 128, 8, 2), ("f16", 128, 4, 4), ("f16", 64, 32, 2),
+    ("f32", 64, 8, 2), ("f32", 128, 8, 1), ("f32", 128, 6, 3),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_parity(gpu_lib, case):
+    dtype, d, hq, hkv = case
+    lay = small_decode(100 + d + hq + hkv, dtype=dtype, batch=7, min_len=1, max_len=700,
+                       num_heads=hq, num_kv_heads=hkv, head_dim=d)
+    _decode_case(lay)
+
+
+def test_tiny_fp32_config(gpu_lib):
+    _decode_case(tiny_decode_fp32())
+
+
+def test_decode_lengths_at_block_edges(gpu_lib):
+    from workloads.layout import build_layout
+    lens = [1, 15, 16, 17, 31, 32, 33, 64, 1024, 1025]
+    lay = build_layout("edges", "bf16", lens, [1] * len(lens), num_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, seed=13, pool_factor=1.1)
+    _decode_case(lay)
+
+
+def test_decode_seq_len_zero_gives_zero(gpu_lib):
+    lay = small_decode(14, dtype="bf16", batch=3, min_len=20, max_len=40)
+    st = materialize(lay, "cuda")
+    gpu_write(st)
+    st.seq_lens[1] = 0
+    out = pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                       lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    assert torch.all(out[1] == 0)
+    assert torch.all(torch.isfinite(out.float()))
+
+
+def test_decode_is_deterministic_and_paging_invariant(gpu_lib):
+    lay = small_decode(15, dtype="bf16", batch=5, min_len=100, max_len=900)
+    st = materialize(lay, "cuda")
+    args = (lay.max_seq_len, lay.scale)
+    a = pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens, *args)
+    b = pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens, *args)
+    # relabel physical blocks: move every block to a new id, rewrite the tables
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    perm = torch.randperm(lay.num_blocks, generator=gen, device="cuda")
+    k2 = torch.empty_like(st.k_cache)
+    v2 = torch.empty_like(st.v_cache)
+    k2[perm] = st.k_cache
+    v2[perm] = st.v_cache
+    table = st.block_table.long()
+    t2 = torch.where(table >= 0, perm[table.clamp(min=0)], table).to(torch.int32).contiguous()
+    c = pa.pa_decode(k2, v2, st.q, t2, st.seq_lens, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+# ------------------------------------------------------------------- split-K
+@pytest.mark.parametrize("dtype,split", [("bf16", 32), ("bf16", 256), ("f16", 48), ("f32", 64)])
+def test_splitk_partials_and_merge(gpu_lib, dtype, split):
+    lay = small_decode(20 + split, dtype=dtype, batch=6, min_len=1, max_len=500,
+                       num_heads=8, num_kv_heads=2, head_dim=128 if dtype != "f32" else 64,
+                       key_outlier_frac=0.05)
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    o_part, lse_part = pa.pa_decode_splitk(st.k_cache, st.v_cache, st.q, st.block_table,
+                                           st.seq_lens, lay.max_seq_len, split, lay.scale)
+    out, lse = pa.pa_lse_merge(o_part, lse_part, st.seq_lens, lay.max_seq_len, split,
+                               out_dtype=st.q.dtype, want_lse=True)
+    torch.cuda.synchronize()
+    s = o_part.shape[2]
+    want_o, want_l = oracle.splitk_partials(snap.q, snap.k, snap.v, lay.block_table,
+                                            lay.seq_lens, lay.scale, lay.block_size,
+                                            lay.dtype, split, s)
+    got_o = o_part.cpu().double().numpy()
+    got_l = lse_part.cpu().double().numpy()
+    empty = np.isneginf(want_l)
+    assert np.array_equal(np.isneginf(got_l), empty), "empty splits must have lse = -inf"
+    assert np.all(got_o[empty] == 0.0)
+    tol = TOL[dtype]
+    assert max_err(got_o[~empty], want_o[~empty]) <= tol
+    assert max_err(got_l[~empty], want_l[~empty]) <= tol
+    want, want_lse = decode_oracle(st, snap, req)
+    err = max_err(gpu_rows(out, lay.dtype), want)
+    print(f"{lay.name} split {split}: merged max|err| = {err:.3e}", flush=True)
+    assert err <= tol
+    assert max_err(lse.cpu().double().numpy(), want_lse) <= tol
+
+
+# -------------------------------------------------------------------- varlen
+VARLEN_CASES = [
+    ("bf16", 128, 8, 2, True), ("bf16", 128, 32, 8, True), ("bf16", 64, 4, 4, True),
+    ("bf16", 128, 8, 1, False), ("f16", 128, 16, 2, True), ("f32", 64, 8, 2, True),
+    ("f32", 128, 4, 4, False),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_varlen_parity(gpu_lib, case):
+    dtype, d, hq, hkv, causal = case
+    lay = small_varlen(200 + d + hq, dtype=dtype, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       prefill=((40, 0), (70, 33), (17, 130), (3, 60), (2, 0)),
+                       decode_lens=(1, 15, 16, 17, 200, 130), shared_prefix_blocks=2,
+                       sharers=(9, 10))
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    check_cache_after_write(st, snap)
+    out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
+                       causal=causal)
+    torch.cuda.synchronize()
+    want, _ = varlen_oracle(st, snap, req, causal=causal)
+    err = max_err(gpu_rows(out, lay.dtype), want)
+    print(f"{lay.name} causal={causal}: varlen max|err| = {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+def test_varlen_all_decode_matches_decode_oracle(gpu_lib):
+    lay = small_decode(30, dtype="bf16", batch=9, min_len=1, max_len=600)
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                       st.block_table, 1, lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    want, _ = decode_oracle(st, snap, req)
+    assert max_err(gpu_rows(out, "bf16"), want) <= TOL["bf16"]
+
+
+def test_varlen_shared_prefix_equals_copied_prefix(gpu_lib):
+    lay = small_varlen(31, dtype="bf16", prefill=((33, 40),), decode_lens=(90, 100, 120),
+                       shared_prefix_blocks=3, sharers=(1, 2, 3))
+    st = materialize(lay, "cuda")
+    gpu_write(st)
+    a = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                     st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale)
+    # copy the shared blocks for request 2 into free blocks and point its table there
+    used = set(int(b) for b in lay.block_table.flatten() if b >= 0)
+    free = [b for b in range(lay.num_blocks) if b not in used][:3]
+    assert len(free) == 3
+    table = st.block_table.clone()
+    for j, fb in enumerate(free):
+        src = int(lay.block_table[2, j])
+        st.k_cache[fb] = st.k_cache[src]
+        st.v_cache[fb] = st.v_cache[src]
+        table[2, j] = fb
+    b = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens, table,
+                     lay.max_query_len, lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------- bad inputs
+def test_binding_rejects_bad_arguments(gpu_lib):
+    lay = small_decode(40, dtype="bf16", batch=2, min_len=10, max_len=20)
+    st = materialize(lay, "cuda")
+    with pytest.raises(ValueError):
+        pa.pa_decode(st.k_cache, st.v_cache, st.q.float(), st.block_table, st.seq_lens,
+                     lay.max_seq_len, lay.scale)
+    with pytest.raises(ValueError):
+        pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table.long(), st.seq_lens,
+                     lay.max_seq_len, lay.scale)
+    with pytest.raises(pa.PaError):
+        # max_seq_len larger than the table can hold
+        pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                     10 ** 6, lay.scale)

@@ -1,0 +1,85 @@
+"""The C ABI library loads and exports what include/pa.h declares, and its
+host-side validation returns the documented status codes (CPU only: none of
+these calls reaches a kernel launch)."""
+
+import ctypes
+import os
+
+import pytest
+
+from paged_kv_cache_221_amd import _native
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_native.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _native.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _native.header_symbols()
+    assert set(names) == set(_native.SIGNATURES), "binding and header disagree"
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def _cache(nb=8, bs=16, hkv=2, d=128, dtype=2, k=1, v=1):
+    return _native.PaKvCache(k, v, nb, bs, hkv, d, dtype)
+
+
+def test_status_strings(lib):
+    for code in range(-6, 1):
+        assert lib.pa_status_str(code)
+    assert lib.pa_status_str(-99) == b"unknown status"
+
+
+def test_splitk_num_splits(lib):
+    assert lib.pa_splitk_num_splits(131072, 2048) == 64
+    assert lib.pa_splitk_num_splits(2049, 2048) == 2
+    assert lib.pa_splitk_num_splits(0, 2048) == 1
+    assert lib.pa_splitk_num_splits(100, 0) == 0
+
+
+def test_validation_codes(lib):
+    byref = ctypes.byref
+    one = ctypes.c_void_p(1)
+    # null cache pointers
+    assert lib.pa_decode(byref(_cache(k=0)), one, one, one, one, 1, 8, 4, 64, 0.1, None) == -1
+    assert lib.pa_decode(None, one, one, one, one, 1, 8, 4, 64, 0.1, None) == -1
+    # null tensors
+    assert lib.pa_decode(byref(_cache()), None, one, one, one, 1, 8, 4, 64, 0.1, None) == -1
+    # heads not a multiple of kv heads
+    assert lib.pa_decode(byref(_cache()), one, one, one, one, 1, 7, 4, 64, 0.1, None) == -2
+    # max_seq_len beyond the table
+    assert lib.pa_decode(byref(_cache()), one, one, one, one, 1, 8, 4, 65, 0.1, None) == -2
+    # non-finite scale
+    assert lib.pa_decode(byref(_cache()), one, one, one, one, 1, 8, 4, 64,
+                         float("nan"), None) == -2
+    # unknown dtype
+    assert lib.pa_decode(byref(_cache(dtype=7)), one, one, one, one, 1, 8, 4, 64, 0.1,
+                         None) == -3
+    # unsupported head_dim / block size / group
+    assert lib.pa_decode(byref(_cache(d=96)), one, one, one, one, 1, 8, 4, 64, 0.1, None) == -4
+    assert lib.pa_decode(byref(_cache(bs=32)), one, one, one, one, 1, 8, 4, 64, 0.1, None) == -4
+    assert lib.pa_decode(byref(_cache(hkv=1)), one, one, one, one, 1, 32, 4, 64, 0.1,
+                         None) == -4
+    # zero requests: nothing to do
+    assert lib.pa_decode(byref(_cache()), None, None, None, None, 0, 8, 4, 64, 0.1, None) == 0
+    # split-K workspace arguments
+    assert lib.pa_decode_splitk(byref(_cache()), one, one, one, one, one, 1, 8, 4, 64, 24,
+                                0.1, None) == -5
+    assert lib.pa_decode_splitk(byref(_cache()), None, one, one, one, one, 1, 8, 4, 64, 32,
+                                0.1, None) == -1
+    assert lib.pa_lse_merge(one, None, one, one, one, 1, 8, 128, 64, 0, 2, None) == -5
+    assert lib.pa_lse_merge(one, None, one, one, one, 1, 8, 128, 64, 32, 9, None) == -3
+    # write: zero tokens is a no-op, null slot mapping is an error
+    assert lib.pa_write_kv(byref(_cache()), None, None, None, 0, None) == 0
+    assert lib.pa_write_kv(byref(_cache()), one, one, None, 4, None) == -1
+    assert lib.pa_write_kv(byref(_cache()), one, one, one, -1, None) == -2
+    # varlen: max_query_len above max_seq_len, bad causal flag
+    assert lib.pa_varlen(byref(_cache()), one, one, one, one, one, 1, 4, 8, 4, 70, 64, 0.1, 1,
+                         None) == -2
+    assert lib.pa_varlen(byref(_cache()), one, one, one, one, one, 1, 4, 8, 4, 4, 64, 0.1, 2,
+                         None) == -2

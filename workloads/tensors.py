@@ -31,7 +31,7 @@ TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat
 RAW_DTYPES = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16}
 NP_RAW = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
 
-_CHUNK_ROWS = 1 << 16
+_CHUNK_ELEMS = 1 << 26   # fp32 temporaries of at most 256 MiB
 
 
 @dataclass
@@ -54,8 +54,9 @@ class StepTensors:
 
 def _randn_into(dst: torch.Tensor, std: float, gen: torch.Generator) -> None:
     flat = dst.view(dst.shape[0], -1)
-    for lo in range(0, flat.shape[0], _CHUNK_ROWS):
-        hi = min(lo + _CHUNK_ROWS, flat.shape[0])
+    rows = max(1, _CHUNK_ELEMS // max(1, flat.shape[1]))
+    for lo in range(0, flat.shape[0], rows):
+        hi = min(lo + rows, flat.shape[0])
         chunk = torch.randn((hi - lo, flat.shape[1]), generator=gen, device=dst.device,
                             dtype=torch.float32)
         if std != 1.0:
@@ -66,8 +67,9 @@ def _randn_into(dst: torch.Tensor, std: float, gen: torch.Generator) -> None:
 def _outliers(dst: torch.Tensor, frac: float, scale: float, gen: torch.Generator) -> None:
     """dst [..., Hkv, D]: scale whole head vectors with probability ``frac``."""
     rows = dst.view(-1, dst.shape[-1])
-    for lo in range(0, rows.shape[0], _CHUNK_ROWS * 8):
-        hi = min(lo + _CHUNK_ROWS * 8, rows.shape[0])
+    step = max(1, _CHUNK_ELEMS // 8)
+    for lo in range(0, rows.shape[0], step):
+        hi = min(lo + step, rows.shape[0])
         pick = torch.rand((hi - lo,), generator=gen, device=dst.device) < frac
         idx = torch.nonzero(pick).squeeze(1) + lo
         if idx.numel():
