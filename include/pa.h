@@ -34,7 +34,8 @@
  *   hints max_seq_len / max_query_len bound every request. The kernels never
  *   read or write outside the buffers described here even when the contract
  *   is broken: an out-of-pool slot is not written, an out-of-pool block id is
- *   read as an empty block, lengths are clipped to max_blocks_per_seq * bs.
+ *   read as zeros (no memory access), lengths are clipped to
+ *   max_blocks_per_seq * bs.
  *   Results for such inputs are unspecified.
  * - Supported now: block_size 16; head_dim 64 or 128; Hq % Hkv == 0 with
  *   Hq / Hkv <= 16; fp32, fp16 and bf16 storage with fp32 accumulation.

@@ -36,26 +36,29 @@ def common_flags():
     ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(jobs: int = 4) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int = 4, extra_flags=(), lib_path: str = LIB_PATH,
+          build_dir: str = BUILD_DIR) -> str:
+    """Compile and link; ``extra_flags`` (e.g. ``-DPA_KV_DEPTH=3``) override
+    the compile-time tunables of the kernels."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as pool:
-        objs = list(pool.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(pool.map(lambda src: _compile(src, build_dir, tuple(extra_flags)), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"linking libpa.so failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -16,6 +16,11 @@
 #include "attn_tile.h"
 #include "pa_launch.h"
 
+// KV blocks each wave keeps in flight (compile-time tunable).
+#ifndef PA_KV_DEPTH
+#define PA_KV_DEPTH 4
+#endif
+
 namespace pa {
 namespace {
 
@@ -42,8 +47,9 @@ __device__ inline void store_chunk(typename Ops<E, D>::storage* dst, const float
   }
 }
 
+// At least two waves per SIMD: 256 registers per lane.
 template <class E, int D, int NW>
-__global__ __launch_bounds__(NW * kWave) void paged_attention_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const AttnArgs a) {
   using O = Ops<E, D>;
   using S = typename O::storage;
   constexpr int kComb = NW > 1 ? NW : 1;
@@ -99,10 +105,14 @@ __global__ __launch_bounds__(NW * kWave) void paged_attention_kernel(const AttnA
     const int nblk = (seq_len + kBlockTokens - 1) / kBlockTokens;
     const int b0 = split * a.split_blocks;
     const int b1 = min(b0 + a.split_blocks, nblk);
-    stream_blocks<E, D>(st, qop, view, b0 + wave, b1, NW, key_end, seq_len, a.scale_log2,
-                        lane);
-    st.l += xor_shuffle(st.l, 16);
-    st.l += xor_shuffle(st.l, 32);
+    // wave w takes the w-th of NW contiguous, nearly equal runs of [b0, b1)
+    const int cnt = max(b1 - b0, 0);
+    const int w_lo = b0 + (int)(((int64_t)cnt * wave) / NW);
+    const int w_hi = b0 + (int)(((int64_t)cnt * (wave + 1)) / NW);
+    stream_blocks<E, D, PA_KV_DEPTH>(st, qop, view, w_lo, w_hi - w_lo, key_end, seq_len,
+                                     a.scale_log2, lane);
+    st.l = sum_xor16(st.l);
+    st.l = sum_xor32(st.l);
 
     const int nrows = n * g;
     auto emit = [&](int rr, int d, float acc, float lsum, float mx) {
@@ -182,10 +192,10 @@ __global__ __launch_bounds__(NW * kWave) void paged_attention_kernel(const AttnA
   O::load_q(qop, qrow, valid, lane);
   const int last = min(tok0 + tpw, n) - 1;
   const int kmax = a.causal ? min(ctx + last + 1, seq_len) : seq_len;
-  stream_blocks<E, D>(st, qop, view, 0, (kmax + kBlockTokens - 1) / kBlockTokens, 1, key_end,
-                      seq_len, a.scale_log2, lane);
-  st.l += xor_shuffle(st.l, 16);
-  st.l += xor_shuffle(st.l, 32);
+  stream_blocks<E, D, PA_KV_DEPTH>(st, qop, view, 0, (kmax + kBlockTokens - 1) / kBlockTokens,
+                                   key_end, seq_len, a.scale_log2, lane);
+  st.l = sum_xor16(st.l);
+  st.l = sum_xor32(st.l);
   if (valid) {
     const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
     S* dst = static_cast<S*>(a.out) + ((int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh) * D +

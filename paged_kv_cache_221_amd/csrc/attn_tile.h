@@ -45,9 +45,49 @@ __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ inline float xor_shuffle(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// max(v[l], v[l ^ 16]) and max(v[l], v[l ^ 32]) with the gfx950 row swaps
+// (VALU only: no LDS traffic, no lgkmcnt wait).
+__device__ inline float max_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float sum_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource over one KV block's slice for one head: base address,
+// byte range (reads at or past it return zeros), gfx9 data-format word.
+using Rsrc = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;
+__device__ inline Rsrc make_rsrc(const void* base, int range_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, range_bytes,
+                                          kRsrcFlags);
+}
+__device__ inline u32x4 buf_load16(Rsrc r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ inline u32x2 buf_load8(Rsrc r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
 // ----------------------------------------------------------- element types
 struct Bf16 {
   using storage = uint16_t;
+  // two floats -> packed bf16 pair (round to nearest even), lo in bits 0..15
+  __device__ static unsigned pack2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 h = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(unsigned, h);
+  }
   __device__ static uint16_t from_float(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
@@ -66,6 +106,11 @@ struct Bf16 {
 
 struct F16 {
   using storage = uint16_t;
+  __device__ static unsigned pack2(float lo, float hi) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 h = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(unsigned, h);
+  }
   __device__ static uint16_t from_float(float f) {
     _Float16 h = (_Float16)f;  // hardware conversion, round to nearest even
     return __builtin_bit_cast(uint16_t, h);
@@ -109,22 +154,31 @@ struct Ops16 {
   };
   using P = u32x2;
 
-  // kblk/vblk point at (key 0 of the block, this KV head, dim 0); rs is the
-  // element stride between consecutive keys (Hkv * D).
-  __device__ static void load(KV& kv, const storage* kblk, const storage* vblk, int64_t rs,
-                              int lane) {
+  // Lane-constant byte offsets of this lane's operand pieces inside a block
+  // slice (rs = elements between consecutive keys, Hkv * D).
+  struct Off {
+    int k[kQk];
+    int v[4];
+  };
+  __device__ static Off offsets(int64_t rs, int lane) {
     const int m = lane & 15, grp = lane >> 4;
+    Off o;
 #pragma unroll
-    for (int c = 0; c < kQk; ++c)
-      kv.k[c] = *reinterpret_cast<const u32x4*>(kblk + m * rs + 32 * c + 8 * grp);
+    for (int c = 0; c < kQk; ++c) o.k[c] = (int)((m * rs + 32 * c + 8 * grp) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.v[i] = (int)(((4 * grp + i) * rs + kVe * m) * 2);
+    return o;
+  }
+  __device__ static void load(KV& kv, Rsrc kr, Rsrc vr, const Off& o) {
+#pragma unroll
+    for (int c = 0; c < kQk; ++c) kv.k[c] = buf_load16(kr, o.k[c]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const storage* src = vblk + (4 * grp + i) * rs + kVe * m;
       if constexpr (kVe == 8) {
-        u32x4 t = *reinterpret_cast<const u32x4*>(src);
+        u32x4 t = buf_load16(vr, o.v[i]);
         kv.v[i].w[0] = t.x; kv.v[i].w[1] = t.y; kv.v[i].w[2] = t.z; kv.v[i].w[3] = t.w;
       } else {
-        u32x2 t = *reinterpret_cast<const u32x2*>(src);
+        u32x2 t = buf_load8(vr, o.v[i]);
         kv.v[i].w[0] = t.x; kv.v[i].w[1] = t.y;
       }
     }
@@ -149,22 +203,19 @@ struct Ops16 {
   }
   __device__ static P pack_p(const float (&p)[4]) {
     P r;
-    r.x = (unsigned)E::from_float(p[0]) | ((unsigned)E::from_float(p[1]) << 16);
-    r.y = (unsigned)E::from_float(p[2]) | ((unsigned)E::from_float(p[3]) << 16);
+    r.x = E::pack2(p[0], p[1]);
+    r.y = E::pack2(p[2], p[3]);
     return r;
   }
   __device__ static void pv(f32x4 (&o)[kChunks], const KV& kv, P p) {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int w = c >> 1;
+      // element c of keys 0,1 (resp. 2,3): low or high halves of word c/2
+      const unsigned sel = (c & 1) == 0 ? 0x05040100u : 0x07060302u;
       u32x2 a;
-      if ((c & 1) == 0) {
-        a.x = (kv.v[0].w[w] & 0xffffu) | (kv.v[1].w[w] << 16);
-        a.y = (kv.v[2].w[w] & 0xffffu) | (kv.v[3].w[w] << 16);
-      } else {
-        a.x = (kv.v[0].w[w] >> 16) | (kv.v[1].w[w] & 0xffff0000u);
-        a.y = (kv.v[2].w[w] >> 16) | (kv.v[3].w[w] & 0xffff0000u);
-      }
+      a.x = __builtin_amdgcn_perm(kv.v[1].w[w], kv.v[0].w[w], sel);
+      a.y = __builtin_amdgcn_perm(kv.v[3].w[w], kv.v[2].w[w], sel);
       o[c] = E::mma_pv(a, p, o[c]);
     }
   }
@@ -195,22 +246,30 @@ struct Ops<F32, D> {
     float p[4];
   };
 
-  __device__ static void load(KV& kv, const storage* kblk, const storage* vblk, int64_t rs,
-                              int lane) {
+  struct Off {
+    int k[kKv];
+    int v[4];
+  };
+  __device__ static Off offsets(int64_t rs, int lane) {
     const int m = lane & 15, grp = lane >> 4;
+    Off o;
 #pragma unroll
-    for (int j = 0; j < kKv; ++j)
-      kv.k[j] = *reinterpret_cast<const f32x4*>(kblk + m * rs + 16 * j + 4 * grp);
+    for (int j = 0; j < kKv; ++j) o.k[j] = (int)((m * rs + 16 * j + 4 * grp) * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const storage* src = vblk + (4 * grp + i) * rs + kVe * m;
+    for (int i = 0; i < 4; ++i) o.v[i] = (int)(((4 * grp + i) * rs + kVe * m) * 4);
+    return o;
+  }
+  __device__ static void load(KV& kv, Rsrc kr, Rsrc vr, const Off& o) {
+#pragma unroll
+    for (int j = 0; j < kKv; ++j) kv.k[j] = __builtin_bit_cast(f32x4, buf_load16(kr, o.k[j]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int w = 0; w < kVe / 4; ++w) {
-        f32x4 t = *reinterpret_cast<const f32x4*>(src + 4 * w);
+        f32x4 t = __builtin_bit_cast(f32x4, buf_load16(vr, o.v[i] + 16 * w));
         kv.v[i][4 * w + 0] = t.x; kv.v[i][4 * w + 1] = t.y;
         kv.v[i][4 * w + 2] = t.z; kv.v[i][4 * w + 3] = t.w;
       }
-    }
   }
   __device__ static void load_q(Q& q, const storage* qrow, bool valid, int lane) {
     const int grp = lane >> 4;
@@ -262,7 +321,7 @@ struct RowState {
   }
 };
 
-// Describes where one wave's KV blocks live.
+// Where one wave's KV blocks live.
 template <class Storage>
 struct KvView {
   const Storage* k;        // k_cache + kv_head * D
@@ -272,20 +331,15 @@ struct KvView {
   int num_blocks;          // pool size, for the out-of-pool guard
 };
 
-// One block: mask, online softmax update, P.V accumulation.
-// key_end: keys >= key_end are invisible to this lane's row.
-// seq_len: keys >= seq_len do not exist (their V may hold anything).
+// One block: mask, online softmax update, P.V accumulation. Keys at or past
+// seq_len were read as zeros (the buffer range stops there); keys at or past
+// key_end are invisible to this lane's row and get probability 0.
 template <class E, int D>
-__device__ inline void consume_block(RowState<D>& st, typename Ops<E, D>::KV& kv,
+__device__ inline void consume_block(RowState<D>& st, const typename Ops<E, D>::KV& kv,
                                      const typename Ops<E, D>::Q& q, int key0, int key_end,
-                                     int seq_len, float scale_log2, int lane) {
+                                     float scale_log2, int lane) {
   using O = Ops<E, D>;
   const int grp = lane >> 4;
-  if (key0 + kBlockTokens > seq_len) {  // wave-uniform: the request's last block
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (key0 + 4 * grp + i >= seq_len) O::zero_v(kv, i);
-  }
   f32x4 acc = O::scores(kv, q);
   float s[4];
 #pragma unroll
@@ -294,8 +348,8 @@ __device__ inline void consume_block(RowState<D>& st, typename Ops<E, D>::KV& kv
     s[i] = key < key_end ? acc[i] * scale_log2 : neg_inf();
   }
   float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  mx = fmaxf(mx, xor_shuffle(mx, 16));
-  mx = fmaxf(mx, xor_shuffle(mx, 32));
+  mx = max_xor16(mx);
+  mx = max_xor32(mx);
   const float m_new = fmaxf(st.m, mx);
   const float m_use = m_new == neg_inf() ? 0.f : m_new;
   // An unchanged maximum (including a row that has seen no key yet) keeps
@@ -313,50 +367,56 @@ __device__ inline void consume_block(RowState<D>& st, typename Ops<E, D>::KV& kv
   O::pv(st.o, kv, O::pack_p(p));
 }
 
-// Streams blocks [b_begin, b_end) with stride b_step through one row tile,
-// loading block n+1 while block n is consumed. All control is wave-uniform.
-template <class E, int D>
+// Streams this wave's contiguous run of n blocks, starting at logical block
+// b_begin, through one row tile. DEPTH blocks are in flight: while block i is
+// consumed, blocks i+1 .. i+DEPTH-1 are loading. Block ids are read with
+// scalar loads; each block is read through a buffer resource whose range ends
+// at the request's last key, so rows past it, blocks whose id is outside the
+// pool and the padding blocks past the run come back as zeros without
+// touching memory. Every iteration loads and consumes unconditionally (a
+// padding block is consumed with no visible key), which lets the compiler wait
+// for exactly the block it consumes instead of draining every load.
+template <class E, int D, int DEPTH>
 __device__ inline void stream_blocks(RowState<D>& st, const typename Ops<E, D>::Q& q,
                                      const KvView<typename Ops<E, D>::storage>& kv_view,
-                                     int b_begin, int b_end, int b_step, int key_end,
-                                     int seq_len, float scale_log2, int lane) {
+                                     int b_begin, int n, int key_end, int seq_len,
+                                     float scale_log2, int lane) {
   using O = Ops<E, D>;
+  using S = typename O::storage;
   using KV = typename O::KV;
-  if (b_begin >= b_end) return;
+  if (n <= 0) return;
+  const typename O::Off off = O::offsets(kv_view.rs, lane);
   const int64_t block_elems = (int64_t)kBlockTokens * kv_view.rs;
-  auto block_id = [&](int b) -> int {
-    int pb = kv_view.table[b];
-    return (pb >= 0 && pb < kv_view.num_blocks) ? pb : -1;
+  const int row_bytes = (int)(kv_view.rs * (int64_t)sizeof(S));
+  const __attribute__((address_space(4))) int32_t* tab =
+      (const __attribute__((address_space(4))) int32_t*)(kv_view.table + b_begin);
+
+  auto load = [&](KV& kv, int i) {
+    const int pb = tab[min(i, n - 1)];
+    const bool ok = i < n && pb >= 0 && pb < kv_view.num_blocks;
+    const int keys = min(seq_len - (b_begin + i) * kBlockTokens, kBlockTokens);
+    const int range = ok ? keys * row_bytes : 0;
+    const int64_t base = (int64_t)(ok ? pb : 0) * block_elems;
+    O::load(kv, make_rsrc(kv_view.k + base, range), make_rsrc(kv_view.v + base, range), off);
   };
-  auto load = [&](KV& kv, int pb) {
-    const int64_t base = (int64_t)(pb < 0 ? 0 : pb) * block_elems;
-    O::load(kv, kv_view.k + base, kv_view.v + base, kv_view.rs, lane);
+  auto consume = [&](const KV& kv, int i) {
+    consume_block<E, D>(st, kv, q, (b_begin + i) * kBlockTokens, i < n ? key_end : 0,
+                        scale_log2, lane);
   };
-  KV buf0, buf1;
-  int b = b_begin;
-  int pb0 = block_id(b);
-  load(buf0, pb0);
-  while (true) {
-    int bn = b + b_step;
-    int pb1 = -1;
-    if (bn < b_end) {
-      pb1 = block_id(bn);
-      load(buf1, pb1);
+
+  KV buf[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) load(buf[j], j);
+  for (int i0 = 0; i0 < n; i0 += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      consume(buf[j], i0 + j);
+      // keep the refill of buf[j] here: the scheduler would otherwise sink
+      // it towards its use and collapse the pipeline
+      __builtin_amdgcn_sched_barrier(0);
+      load(buf[j], i0 + j + DEPTH);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (pb0 >= 0)
-      consume_block<E, D>(st, buf0, q, b * kBlockTokens, key_end, seq_len, scale_log2, lane);
-    if (bn >= b_end) break;
-    b = bn;
-    bn = b + b_step;
-    pb0 = -1;
-    if (bn < b_end) {
-      pb0 = block_id(bn);
-      load(buf0, pb0);
-    }
-    if (pb1 >= 0)
-      consume_block<E, D>(st, buf1, q, b * kBlockTokens, key_end, seq_len, scale_log2, lane);
-    if (bn >= b_end) break;
-    b = bn;
   }
 }
 

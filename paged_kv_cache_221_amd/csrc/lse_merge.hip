@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kMergeWaves* kWave) void lse_merge_kernel(const Mer
   const float* lse = a.lse_part + unit * a.num_splits;
   const float* op = a.o_part + unit * a.num_splits * a.head_dim;
 
+  // Pass 1: the largest split LSE and the sum of weights; lane s holds split s.
   float mx = neg_inf();
   for (int s = lane; s < ns; s += kWave) mx = fmaxf(mx, lse[s]);
   mx = wave_max(mx);
@@ -51,10 +52,24 @@ __global__ __launch_bounds__(kMergeWaves* kWave) void lse_merge_kernel(const Mer
   for (int s = lane; s < ns; s += kWave) tot += fast_exp2((lse[s] - mu) * kLog2e);
   tot = wave_sum(tot);
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  for (int d = lane; d < a.head_dim; d += kWave) {
+
+  // Pass 2: lanes over head_dim; splits in chunks of 64, the weight of split
+  // s0 + j read from lane j (readlane ignores the exec mask).
+  for (int d0 = 0; d0 < a.head_dim; d0 += kWave) {
+    const int d = d0 + lane;
+    const bool live = d < a.head_dim;
     float acc = 0.f;
-    for (int s = 0; s < ns; ++s) acc += fast_exp2((lse[s] - mu) * kLog2e) * op[(int64_t)s * a.head_dim + d];
-    put<E>(a.out, unit * a.head_dim + d, acc * inv);
+    for (int s0 = 0; s0 < ns; s0 += kWave) {
+      const int sl = s0 + lane;
+      const float w = sl < ns ? fast_exp2((lse[sl] - mu) * kLog2e) * inv : 0.f;
+      const int cnt = min(kWave, ns - s0);
+#pragma unroll 8
+      for (int j = 0; j < cnt; ++j) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+        if (live) acc += wj * op[(int64_t)(s0 + j) * a.head_dim + d];
+      }
+    }
+    if (live) put<E>(a.out, unit * a.head_dim + d, acc);
   }
   if (a.lse_out != nullptr && lane == 0)
     a.lse_out[unit] = tot > 0.f ? mx + fast_log2(tot) * kLn2 : neg_inf();

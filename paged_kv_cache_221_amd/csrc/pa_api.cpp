@@ -62,6 +62,9 @@ AttnArgs base_args(const pa_kv_cache* c, const void* q, const int32_t* block_tab
 // Waves per workgroup for a single-tile (decode-like) unit covering
 // `blocks` KV blocks: more waves give a long split more loads in flight.
 int decode_waves(int blocks) {
+#ifdef PA_DECODE_WAVES
+  if (blocks >= 0) return PA_DECODE_WAVES;
+#endif
   if (blocks >= 64) return 4;
   if (blocks >= 16) return 2;
   return 1;
