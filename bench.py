@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged GQA decode: achieved HBM GB/s (% of peak) + decode tokens/s per layer"
 PEAK_HBM_GBS = 8000.0
-ATTN_SOURCES = ["attention.hip", "attn_tile.h", "pa_api.cpp"]
+ATTN_SOURCES = ["attention.hip", "balanced.hip", "attn_tile.h", "pa_api.cpp"]
 
 
 def kernel_source_hash() -> str:
@@ -93,6 +93,10 @@ class DecodeStep:
         self.st, self.path, self.split = st, path, split_tokens
         lay = st.layout
         self.out = torch.empty_like(st.q)
+        if path == "balanced":
+            n = pa.pa_decode_balanced_workspace_bytes(st.k_cache, st.v_cache, lay.num_seqs,
+                                                      lay.num_heads)
+            self.ws = torch.zeros(n, dtype=torch.uint8, device=st.q.device)
         if path == "splitk":
             s = pa.pa_splitk_num_splits(lay.max_seq_len, split_tokens)
             b, hq, d = st.q.shape
@@ -107,6 +111,11 @@ class DecodeStep:
         if self.path == "decode":
             pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
                          lay.max_seq_len, lay.scale, out=self.out)
+            if ev is not None:
+                ev[1].record()
+        elif self.path == "balanced":
+            pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                                  lay.max_seq_len, lay.scale, workspace=self.ws, out=self.out)
             if ev is not None:
                 ev[1].record()
         else:
@@ -240,7 +249,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--path", choices=["decode", "splitk"], default="decode")
+    ap.add_argument("--path", choices=["decode", "balanced", "splitk"], default="balanced")
     ap.add_argument("--split-tokens", type=int, default=512)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=10.0)

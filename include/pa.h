@@ -17,8 +17,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every tensor pointer is DEVICE memory owned by the caller. The library
- *   allocates nothing, never synchronises, keeps no mutable global state and
- *   may be called from several host threads at once.
+ *   allocates nothing, never synchronises and may be called from several host
+ *   threads at once; its only global state is a per-device cache of kernel
+ *   occupancy, filled on first use.
  * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *   NULL means the null stream). Results are ready when the stream is.
  * - Tensors are dense and row-major with exactly the shapes written in the
@@ -132,6 +133,30 @@ pa_status pa_lse_merge(void *out, float *lse_out, const float *o_part,
                        const float *lse_part, const int32_t *seq_lens, int num_seqs,
                        int num_heads, int head_dim, int max_seq_len, int split_tokens,
                        pa_dtype out_dtype, void *stream);
+
+/* Balanced paged decode [P1 §04; P1 §07]: the same result as pa_decode, for
+ * batches of ragged lengths. The batch's work -- every (request, KV head,
+ * 16-token block) in request-major order -- is cut into one equal contiguous
+ * share per wave the GPU can hold at once, so short requests do not leave the
+ * GPU idle while the longest ones finish. A share's end that cuts a
+ * (request, KV head) is written as a partial (softmax-normalised output and
+ * log-sum-exp) and a second kernel renormalises the partials, as the
+ * Flash-Decoding merge of [P1 §07] does, with split points chosen for
+ * balance. Two kernels are launched on `stream`.
+ *   workspace       : caller-owned device memory of at least
+ *                     pa_decode_balanced_workspace_bytes(...) bytes; its
+ *                     contents need not be initialised; two calls in flight
+ *                     at once must not share it
+ *   num_seqs        : at most 4096 (else PA_ERR_UNSUPPORTED)
+ * Other arguments as for pa_decode. Too small a workspace returns
+ * PA_ERR_WORKSPACE. */
+size_t pa_decode_balanced_workspace_bytes(const pa_kv_cache *cache, int num_seqs,
+                                          int num_heads);
+pa_status pa_decode_balanced(const pa_kv_cache *cache, void *out, const void *q,
+                             const int32_t *block_table, const int32_t *seq_lens,
+                             int num_seqs, int num_heads, int max_blocks_per_seq,
+                             int max_seq_len, float scale, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* Varlen mixed step [P1 §03/§04 flattened batch and cu_seqlens; P1 §07
  * chunked prefill]: request r owns query rows [cu[r], cu[r+1]) of the

@@ -10,6 +10,8 @@ from .api import (  # noqa: F401
     PaError,
     kv_cache_struct,
     pa_decode,
+    pa_decode_balanced,
+    pa_decode_balanced_workspace_bytes,
     pa_decode_splitk,
     pa_lse_merge,
     pa_splitk_num_splits,

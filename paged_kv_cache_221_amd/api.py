@@ -111,6 +111,38 @@ def pa_decode(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int, scal
     return out
 
 
+def pa_decode_balanced_workspace_bytes(k_cache, v_cache, num_seqs: int, num_heads: int) -> int:
+    c = kv_cache_struct(k_cache, v_cache)
+    return int(_native.load().pa_decode_balanced_workspace_bytes(ctypes.byref(c), int(num_seqs),
+                                                                 int(num_heads)))
+
+
+def pa_decode_balanced(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int,
+                       scale: float, workspace=None, out=None):
+    """Balanced decode; ``workspace`` is a uint8 GPU tensor of at least
+    ``pa_decode_balanced_workspace_bytes`` bytes (allocated here if None); its
+    contents need not be initialised."""
+    lib = _native.load()
+    c = kv_cache_struct(k_cache, v_cache)
+    _dev(q, "q", k_cache.dtype)
+    if q.dim() != 3 or q.shape[2] != c.head_dim:
+        raise ValueError("q must be [num_seqs, Hq, D]")
+    b, hq, _ = q.shape
+    max_blocks = _attention_meta(c, block_table, seq_lens, b)
+    need = pa_decode_balanced_workspace_bytes(k_cache, v_cache, b, hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check("pa_decode_balanced", lib.pa_decode_balanced(
+        ctypes.byref(c), _ptr(out), _ptr(q), _ptr(block_table), _ptr(seq_lens), b, hq,
+        max_blocks, int(max_seq_len), float(scale), _ptr(workspace), workspace.numel(),
+        _stream(q)))
+    return out
+
+
 def pa_splitk_num_splits(max_seq_len: int, split_tokens: int) -> int:
     return int(_native.load().pa_splitk_num_splits(int(max_seq_len), int(split_tokens)))
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
-SOURCES = ["attention.hip", "write_kv.hip", "lse_merge.hip", "pa_api.cpp"]
+SOURCES = ["attention.hip", "balanced.hip", "write_kv.hip", "lse_merge.hip", "pa_api.cpp"]
 ARCH = "gfx950"
 
 

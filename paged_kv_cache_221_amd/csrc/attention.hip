@@ -16,36 +16,9 @@
 #include "attn_tile.h"
 #include "pa_launch.h"
 
-// KV blocks each wave keeps in flight (compile-time tunable).
-#ifndef PA_KV_DEPTH
-#define PA_KV_DEPTH 4
-#endif
 
 namespace pa {
 namespace {
-
-template <class E, int D>
-__device__ inline void store_chunk(typename Ops<E, D>::storage* dst, const float* v) {
-  constexpr int n = D / 16;
-  using S = typename Ops<E, D>::storage;
-  if constexpr (sizeof(S) == 2) {
-    unsigned w[n / 2];
-#pragma unroll
-    for (int j = 0; j < n / 2; ++j)
-      w[j] = (unsigned)Ops<E, D>::to_storage(v[2 * j]) |
-             ((unsigned)Ops<E, D>::to_storage(v[2 * j + 1]) << 16);
-    if constexpr (n == 8) {
-      *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
-    } else {
-      *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < n / 4; ++j)
-      *reinterpret_cast<f32x4*>(dst + 4 * j) = f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2],
-                                                    v[4 * j + 3]};
-  }
-}
 
 // At least two waves per SIMD: 256 registers per lane.
 template <class E, int D, int NW>
@@ -109,7 +82,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const At
     const int cnt = max(b1 - b0, 0);
     const int w_lo = b0 + (int)(((int64_t)cnt * wave) / NW);
     const int w_hi = b0 + (int)(((int64_t)cnt * (wave + 1)) / NW);
-    stream_blocks<E, D, PA_KV_DEPTH>(st, qop, view, w_lo, w_hi - w_lo, key_end, seq_len,
+    stream_blocks<E, D, kv_depth<E>()>(st, qop, view, w_lo, w_hi - w_lo, key_end, seq_len,
                                      a.scale_log2, lane);
     st.l = sum_xor16(st.l);
     st.l = sum_xor32(st.l);
@@ -192,7 +165,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const At
   O::load_q(qop, qrow, valid, lane);
   const int last = min(tok0 + tpw, n) - 1;
   const int kmax = a.causal ? min(ctx + last + 1, seq_len) : seq_len;
-  stream_blocks<E, D, PA_KV_DEPTH>(st, qop, view, 0, (kmax + kBlockTokens - 1) / kBlockTokens,
+  stream_blocks<E, D, kv_depth<E>()>(st, qop, view, 0, (kmax + kBlockTokens - 1) / kBlockTokens,
                                    key_end, seq_len, a.scale_log2, lane);
   st.l = sum_xor16(st.l);
   st.l = sum_xor32(st.l);

@@ -307,6 +307,40 @@ struct Ops<F32, D> {
   __device__ static storage to_storage(float f) { return f; }
 };
 
+// Stores D/16 consecutive output values of one row in the storage dtype.
+template <class E, int D>
+__device__ inline void store_chunk(typename Ops<E, D>::storage* dst, const float* v) {
+  constexpr int n = D / 16;
+  using S = typename Ops<E, D>::storage;
+  if constexpr (sizeof(S) == 2) {
+    unsigned w[n / 2];
+#pragma unroll
+    for (int j = 0; j < n / 2; ++j)
+      w[j] = (unsigned)Ops<E, D>::to_storage(v[2 * j]) |
+             ((unsigned)Ops<E, D>::to_storage(v[2 * j + 1]) << 16);
+    if constexpr (n == 8) {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < n / 4; ++j)
+      *reinterpret_cast<f32x4*>(dst + 4 * j) = f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2],
+                                                    v[4 * j + 3]};
+  }
+}
+
+// KV blocks each wave keeps in flight. fp32 operands are twice the size, so
+// they get half the depth to stay within the register budget.
+#ifndef PA_KV_DEPTH
+#define PA_KV_DEPTH 4
+#endif
+template <class E>
+constexpr int kv_depth() {
+  return sizeof(typename E::storage) == 4 ? 2 : PA_KV_DEPTH;
+}
+
 // ------------------------------------------------------------ row tile state
 template <int D>
 struct RowState {

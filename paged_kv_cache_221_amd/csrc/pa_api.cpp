@@ -3,6 +3,8 @@
 // device memory or synchronises.
 #include <math.h>
 
+#include <atomic>
+
 #include "pa_launch.h"
 
 namespace {
@@ -68,6 +70,50 @@ int decode_waves(int blocks) {
   if (blocks >= 64) return 4;
   if (blocks >= 16) return 2;
   return 1;
+}
+
+// Resident waves of the balanced kernel, cached per (device, dtype, head_dim):
+// the value depends only on the compiled kernel and the device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_total_waves[kMaxDevices][3][2];
+struct TotalWavesInit {
+  TotalWavesInit() {
+    for (auto& d : g_total_waves)
+      for (auto& t : d)
+        for (auto& v : t) v.store(-1);
+  }
+} g_total_waves_init;
+
+int total_waves(pa_dtype dtype, int head_dim) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev >= kMaxDevices) return pa::balanced_total_waves(dtype, head_dim);
+  std::atomic<int>& slot = g_total_waves[dev][(int)dtype][head_dim == 128 ? 1 : 0];
+  int v = slot.load();
+  if (v < 0) {
+    v = pa::balanced_total_waves(dtype, head_dim);
+    slot.store(v);
+  }
+  return v;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BalancedLayout {
+  size_t records, part_o, part_lse, total;
+};
+
+// Piece slots: at most total_waves + (segments) of them, each `group` rows.
+BalancedLayout balanced_layout(int tw, int group, int head_dim, int num_seqs,
+                               int num_kv_heads) {
+  const size_t segs = (size_t)num_seqs * num_kv_heads;
+  const size_t slots = (size_t)tw + segs;
+  BalancedLayout l;
+  l.records = 0;
+  l.part_o = align256(segs * 2 * sizeof(int32_t));
+  l.part_lse = l.part_o + align256(slots * group * head_dim * sizeof(float));
+  l.total = l.part_lse + align256(slots * group * sizeof(float));
+  return l;
 }
 
 }  // namespace
@@ -211,6 +257,61 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
   if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
   return launched(pa::launch_attention(a, cache->dtype, cache->head_dim, waves, grid,
                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_balanced_workspace_bytes(const pa_kv_cache* cache, int num_seqs,
+                                          int num_heads) {
+  if (check_cache(cache) != PA_OK || num_seqs < 0 || num_heads <= 0 ||
+      num_heads % cache->num_kv_heads != 0)
+    return 0;
+  if (cache->head_dim != 64 && cache->head_dim != 128) return 0;
+  const int tw = total_waves(cache->dtype, cache->head_dim);
+  if (tw <= 0) return 0;
+  return balanced_layout(tw, num_heads / cache->num_kv_heads, cache->head_dim, num_seqs,
+                         cache->num_kv_heads)
+      .total;
+}
+
+pa_status pa_decode_balanced(const pa_kv_cache* cache, void* out, const void* q,
+                             const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
+                             int num_heads, int max_blocks_per_seq, int max_seq_len, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  s = check_attention_shape(cache, num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale);
+  if (s != PA_OK) return s;
+  if (num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (out == nullptr || q == nullptr || block_table == nullptr || seq_lens == nullptr)
+    return PA_ERR_NULL;
+  const int tw = total_waves(cache->dtype, cache->head_dim);
+  if (tw <= 0) return PA_ERR_LAUNCH;
+  const int group = num_heads / cache->num_kv_heads;
+  const BalancedLayout lay =
+      balanced_layout(tw, group, cache->head_dim, num_seqs, cache->num_kv_heads);
+  if (workspace == nullptr) return PA_ERR_NULL;
+  if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  pa::BalancedArgs a{};
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.q = q;
+  a.out = out;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+  a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
+  a.records = reinterpret_cast<int2*>(ws + lay.records);
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = group;
+  a.head_dim = cache->head_dim;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.total_waves = tw;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return launched(pa::launch_balanced(a, cache->dtype, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

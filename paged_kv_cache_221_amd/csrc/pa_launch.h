@@ -46,6 +46,30 @@ struct MergeArgs {
   int split_tokens;
 };
 
+// Balanced decode: the batch's (request, KV head, block) items in equal
+// shares, one per resident wave.
+constexpr int kMaxBalancedSeqs = 4096;
+struct BalancedArgs {
+  const void* k_cache;
+  const void* v_cache;
+  const void* q;              // [B, Hq, D]
+  void* out;                  // [B, Hq, D]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* part_o;              // [total_waves + B*Hkv, group, D] partial outputs
+  float* part_lse;            // [total_waves + B*Hkv, group] partial LSEs (log2 domain)
+  int2* records;              // [B, Hkv] (first piece slot, piece count; 0 = no merge)
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int group;
+  int head_dim;
+  int num_blocks;
+  int max_blocks;
+  int total_waves;
+  float scale_log2;
+};
+
 // Waves per workgroup the attention kernel is built for.
 constexpr int kAttnWaves[] = {1, 2, 4};
 
@@ -54,5 +78,8 @@ hipError_t launch_write_kv(const pa_kv_cache* cache, const void* k_new, const vo
 hipError_t launch_attention(const AttnArgs& args, pa_dtype dtype, int head_dim, int waves,
                             int64_t grid, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& args, pa_dtype out_dtype, hipStream_t stream);
+// Resident waves of the balanced decode kernel on the current device (0 on error).
+int balanced_total_waves(pa_dtype dtype, int head_dim);
+hipError_t launch_balanced(const BalancedArgs& args, pa_dtype dtype, hipStream_t stream);
 
 }  // namespace pa

@@ -77,7 +77,7 @@ def test_tiny_decode_fp32_full():
     _decode_check(st, snap, req, out)
 
 
-@pytest.mark.parametrize("path", ["splitk", "decode"])
+@pytest.mark.parametrize("path", ["balanced", "splitk", "decode"])
 def test_llama3_8b_decode_full(path):
     lay = llama3_8b_decode()
     st = materialize(lay, "cuda")
@@ -86,6 +86,9 @@ def test_llama3_8b_decode_full(path):
     if path == "decode":
         out = pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
                            lay.max_seq_len, lay.scale)
+    elif path == "balanced":
+        out = pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                                    lay.max_seq_len, lay.scale)
     else:
         o, l = pa.pa_decode_splitk(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
                                    lay.max_seq_len, BENCH_SPLIT_TOKENS, lay.scale)
@@ -114,13 +117,26 @@ def test_long_context_splitk_sampled():
     assert nonempty == 344
 
 
-def test_llama2_7b_mha_decode_sampled():
+def test_long_context_balanced_sampled():
+    lay = long_context_splitk()
+    st = materialize(lay, "cuda")
+    req = [0, 3, 7]
+    snap = _write_and_check(st, req)
+    out = pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                                lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    _decode_check(st, snap, req, out)
+
+
+@pytest.mark.parametrize("path", ["decode", "balanced"])
+def test_llama2_7b_mha_decode_sampled(path):
     lay = llama2_7b_mha_decode()
     st = materialize(lay, "cuda")
     req = _sample(lay, 6, 44)
     snap = _write_and_check(st, req)
-    out = pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
-                       lay.max_seq_len, lay.scale)
+    fn = pa.pa_decode if path == "decode" else pa.pa_decode_balanced
+    out = fn(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens, lay.max_seq_len,
+             lay.scale)
     torch.cuda.synchronize()
     _decode_check(st, snap, req, out)
 

@@ -125,6 +125,59 @@ def test_decode_is_deterministic_and_paging_invariant(gpu_lib):
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+# ------------------------------------------------------------ balanced decode
+BALANCED_CASES = [
+    # dtype, head_dim, Hq, Hkv, batch, max_len
+    ("bf16", 128, 32, 8, 9, 2000), ("bf16", 128, 8, 2, 3, 40), ("bf16", 64, 8, 8, 12, 700),
+    ("f16", 128, 32, 32, 5, 900), ("f16", 128, 16, 1, 7, 1500), ("f32", 64, 8, 2, 6, 500),
+    ("f32", 128, 6, 3, 4, 300),
+]
+
+
+@pytest.mark.parametrize("case", BALANCED_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_balanced_decode_parity(gpu_lib, case):
+    dtype, d, hq, hkv, batch, max_len = case
+    lay = small_decode(300 + d + hq + batch, dtype=dtype, batch=batch, min_len=1,
+                       max_len=max_len, num_heads=hq, num_kv_heads=hkv, head_dim=d)
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    out = pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                                lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    want, _ = decode_oracle(st, snap, req)
+    err = max_err(gpu_rows(out, dtype), want)
+    print(f"{lay.name}: balanced max|err| = {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+def test_balanced_decode_empty_requests_and_reuse(gpu_lib):
+    lay = small_decode(41, dtype="bf16", batch=8, min_len=50, max_len=3000, num_heads=32,
+                       num_kv_heads=8)
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    ws = torch.empty(pa.pa_decode_balanced_workspace_bytes(st.k_cache, st.v_cache, 8, 32),
+                     dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)   # stale contents must not matter
+    lens = st.seq_lens.clone()
+    lens[[0, 3, 7]] = 0
+    out = pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table, lens,
+                                lay.max_seq_len, lay.scale, workspace=ws)
+    again = pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table, lens,
+                                  lay.max_seq_len, lay.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    for r in (0, 3, 7):
+        assert torch.all(out[r] == 0)
+    keep = [r for r in req if r not in (0, 3, 7)]
+    want, _ = decode_oracle(st, snap, keep)
+    assert max_err(gpu_rows(out, "bf16")[keep], want[keep]) <= TOL["bf16"]
+    with pytest.raises(pa.PaError):
+        pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table, lens,
+                              lay.max_seq_len, lay.scale, workspace=ws[:16])
+
+
 # ------------------------------------------------------------------- split-K
 @pytest.mark.parametrize("dtype,split", [("bf16", 32), ("bf16", 256), ("f16", 48), ("f32", 64)])
 def test_splitk_partials_and_merge(gpu_lib, dtype, split):

@@ -83,3 +83,18 @@ def test_validation_codes(lib):
                          None) == -2
     assert lib.pa_varlen(byref(_cache()), one, one, one, one, one, 1, 4, 8, 4, 4, 64, 0.1, 2,
                          None) == -2
+
+
+def test_balanced_validation_codes(lib):
+    byref = ctypes.byref
+    one = ctypes.c_void_p(1)
+    # more requests than the balanced kernel's prefix buffer holds
+    assert lib.pa_decode_balanced(byref(_cache()), one, one, one, one, 5000, 8, 4, 64, 0.1,
+                                  one, 1 << 30, None) == -4
+    # zero requests: nothing to do, workspace not needed
+    assert lib.pa_decode_balanced(byref(_cache()), None, None, None, None, 0, 8, 4, 64, 0.1,
+                                  None, 0, None) == 0
+    assert lib.pa_decode_balanced(byref(_cache(d=96)), one, one, one, one, 1, 8, 4, 64, 0.1,
+                                  one, 1 << 30, None) == -4
+    assert lib.pa_decode_balanced_workspace_bytes(None, 4, 8) == 0
+    assert lib.pa_decode_balanced_workspace_bytes(byref(_cache()), 4, 7) == 0
