@@ -71,14 +71,24 @@ def varlen_bytes(layout) -> int:
     return int(lens.sum() * kvb + qo + 4 * blocks.sum() + 4 * (2 * layout.num_seqs + 1))
 
 
-def load_traffic(src_hash: str):
+# Kernels launched by the timed attention call of each path.
+PATH_KERNELS = {
+    "decode": "paged_attention_kernel",
+    "balanced": "balanced_decode_kernel + balanced_merge_kernel",
+    "splitk": "paged_attention_kernel (split-K partials)",
+}
+
+
+def load_traffic(src_hash: str, path_name: str):
+    """HBM bytes per attention call from the committed counter summary, if it
+    was taken on the current kernel sources and the same path."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != src_hash:
+    if t.get("kernel_source_hash") != src_hash or t.get("path") != path_name:
         return None
     return t.get("bytes_per_launch")
 
@@ -256,6 +266,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run torch's elementwise negation over this many MiB of "
+                         "fp32 (3 times): a kernel that reads and writes a known number of "
+                         "bytes, for scaling HBM counter readings")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -277,6 +291,15 @@ def main():
     pa.load()
     torch.cuda.set_device(0)
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     layout = llama3_8b_decode()
     copies = [materialize(layout, "cuda", seed_offset=i) for i in range(args.copies)]
     steps = [DecodeStep(st, args.path, args.split_tokens) for st in copies]
@@ -293,7 +316,7 @@ def main():
     value = step_bytes / (step_ms * 1e-3) / 1e9
     achieved = dec_b / (kern_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = load_traffic(src_hash)
+    traffic = load_traffic(src_hash, args.path)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -320,7 +343,7 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": "paged_attention_kernel",
+                     "traffic": traffic, "kernel": PATH_KERNELS[args.path],
                      "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": dec_b,
                      "kernel_source_hash": src_hash},
     }
