@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
-SOURCES = ["attention.hip", "balanced.hip", "write_kv.hip", "lse_merge.hip", "pa_api.cpp"]
+SOURCES = ["attention.hip", "balanced.hip", "prefill.hip", "write_kv.hip", "lse_merge.hip",
+           "pa_api.cpp"]
 ARCH = "gfx950"
 
 
@@ -32,6 +33,10 @@ def common_flags():
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep MFMA accumulators in VGPRs: with AGPR accumulators the prefill
+        # kernel's conditional rescale made the compiler mirror all of them
+        # through VGPRs on every block
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
     ]
 

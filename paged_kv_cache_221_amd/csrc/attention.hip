@@ -8,9 +8,7 @@
 //   blocks of the split and their partial softmax states are merged through
 //   LDS at the end. Decode streams the whole KV from HBM, so this is the
 //   bandwidth-bound path ([P1 §04], [P3 §1.2]).
-// - A longer query (chunked prefill, [P1 §07]) is cut into tiles; each wave
-//   owns 16 rows (tokens x heads of one KV group) and streams every KV block
-//   its rows can see under the causal mask.
+// - A longer query (chunked prefill, [P1 §07]) is left to prefill.hip.
 // Split-K (Flash-Decoding, [P1 §07]) writes each split's normalised output
 // and its natural-log LSE; pa_lse_merge renormalises them.
 #include "attn_tile.h"
@@ -66,7 +64,9 @@ __global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const At
   RowState<D> st;
   st.init();
 
-  if (n * g <= 16) {
+  // A query longer than one 16-row tile is a prefill chunk: prefill.hip.
+  if (n * g > 16) return;
+  {
     // ---------------------------------------------------- single-tile unit
     if (tile != 0 || n == 0) return;
     const int tok = row / g, hh = row - (row / g) * g;
@@ -153,34 +153,6 @@ __global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const At
     return;
   }
 
-  // ----------------------------------------------------------- tiled prefill
-  const int tpw = 16 / g;  // query tokens per wave
-  const int tok0 = (tile * NW + wave) * tpw;
-  if (tok0 >= n) return;
-  const int tok = tok0 + row / g, hh = row - (row / g) * g;
-  const bool valid = row < tpw * g && tok < n;
-  const int key_end = !valid ? 0 : (a.causal ? min(ctx + tok + 1, seq_len) : seq_len);
-  const S* qrow = static_cast<const S*>(a.q) +
-                  ((int64_t)(q_lo + (valid ? tok : 0)) * a.num_heads + kvh * g + hh) * D;
-  O::load_q(qop, qrow, valid, lane);
-  const int last = min(tok0 + tpw, n) - 1;
-  const int kmax = a.causal ? min(ctx + last + 1, seq_len) : seq_len;
-  stream_blocks<E, D, kv_depth<E>()>(st, qop, view, 0, (kmax + kBlockTokens - 1) / kBlockTokens,
-                                   key_end, seq_len, a.scale_log2, lane);
-  st.l = sum_xor16(st.l);
-  st.l = sum_xor32(st.l);
-  if (valid) {
-    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-    S* dst = static_cast<S*>(a.out) + ((int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh) * D +
-             (D / 4) * grp;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v[D / 16];
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) v[c] = st.o[c][i] * inv;
-      store_chunk<E, D>(dst + (D / 16) * i, v);
-    }
-  }
 }
 
 template <class E, int D>

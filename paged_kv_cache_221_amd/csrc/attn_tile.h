@@ -183,6 +183,26 @@ struct Ops16 {
       }
     }
   }
+  // Same operand layout, read from a block staged in LDS: rows of `row_bytes`
+  // bytes, K rows then V rows in separate arrays.
+  __device__ static void load_lds(KV& kv, const char* kb, const char* vb, int row_bytes,
+                                  int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < kQk; ++c)
+      kv.k[c] = *reinterpret_cast<const u32x4*>(kb + m * row_bytes + (32 * c + 8 * grp) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const char* src = vb + (4 * grp + i) * row_bytes + kVe * m * 2;
+      if constexpr (kVe == 8) {
+        u32x4 t = *reinterpret_cast<const u32x4*>(src);
+        kv.v[i].w[0] = t.x; kv.v[i].w[1] = t.y; kv.v[i].w[2] = t.z; kv.v[i].w[3] = t.w;
+      } else {
+        u32x2 t = *reinterpret_cast<const u32x2*>(src);
+        kv.v[i].w[0] = t.x; kv.v[i].w[1] = t.y;
+      }
+    }
+  }
   __device__ static void load_q(Q& q, const storage* qrow, bool valid, int lane) {
     const int grp = lane >> 4;
 #pragma unroll
@@ -207,18 +227,27 @@ struct Ops16 {
     r.y = E::pack2(p[2], p[3]);
     return r;
   }
-  __device__ static void pv(f32x4 (&o)[kChunks], const KV& kv, P p) {
+  // The PV A operands of a block, one per 16-dim chunk: element c of each of
+  // the lane's four key rows (low or high halves of word c/2).
+  struct VA {
+    u32x2 a[kChunks];
+  };
+  __device__ static VA build_v(const KV& kv) {
+    VA va;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int w = c >> 1;
-      // element c of keys 0,1 (resp. 2,3): low or high halves of word c/2
       const unsigned sel = (c & 1) == 0 ? 0x05040100u : 0x07060302u;
-      u32x2 a;
-      a.x = __builtin_amdgcn_perm(kv.v[1].w[w], kv.v[0].w[w], sel);
-      a.y = __builtin_amdgcn_perm(kv.v[3].w[w], kv.v[2].w[w], sel);
-      o[c] = E::mma_pv(a, p, o[c]);
+      va.a[c].x = __builtin_amdgcn_perm(kv.v[1].w[w], kv.v[0].w[w], sel);
+      va.a[c].y = __builtin_amdgcn_perm(kv.v[3].w[w], kv.v[2].w[w], sel);
     }
+    return va;
   }
+  __device__ static void pv_with(f32x4 (&o)[kChunks], const VA& va, P p) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) o[c] = E::mma_pv(va.a[c], p, o[c]);
+  }
+  __device__ static void pv(f32x4 (&o)[kChunks], const KV& kv, P p) { pv_with(o, build_v(kv), p); }
   __device__ static storage to_storage(float f) { return E::from_float(f); }
 };
 
@@ -271,6 +300,22 @@ struct Ops<F32, D> {
         kv.v[i][4 * w + 2] = t.z; kv.v[i][4 * w + 3] = t.w;
       }
   }
+  __device__ static void load_lds(KV& kv, const char* kb, const char* vb, int row_bytes,
+                                  int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < kKv; ++j)
+      kv.k[j] = *reinterpret_cast<const f32x4*>(kb + m * row_bytes + (16 * j + 4 * grp) * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int w = 0; w < kVe / 4; ++w) {
+        f32x4 t = *reinterpret_cast<const f32x4*>(vb + (4 * grp + i) * row_bytes +
+                                                  (kVe * m + 4 * w) * 4);
+        kv.v[i][4 * w + 0] = t.x; kv.v[i][4 * w + 1] = t.y;
+        kv.v[i][4 * w + 2] = t.z; kv.v[i][4 * w + 3] = t.w;
+      }
+  }
   __device__ static void load_q(Q& q, const storage* qrow, bool valid, int lane) {
     const int grp = lane >> 4;
 #pragma unroll
@@ -296,6 +341,24 @@ struct Ops<F32, D> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.p[i] = p[i];
     return r;
+  }
+  struct VA {
+    float v[4][kVe];
+  };
+  __device__ static VA build_v(const KV& kv) {
+    VA va;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < kVe; ++e) va.v[i][e] = kv.v[i][e];
+    return va;
+  }
+  __device__ static void pv_with(f32x4 (&o)[kChunks], const VA& va, const P& p) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.v[i][c], p.p[i], o[c], 0, 0, 0);
   }
   __device__ static void pv(f32x4 (&o)[kChunks], const KV& kv, const P& p) {
 #pragma unroll
@@ -344,7 +407,7 @@ constexpr int kv_depth() {
 // ------------------------------------------------------------ row tile state
 template <int D>
 struct RowState {
-  float m;  // running max of the row's scores, log2 domain (replicated per row)
+  float m;  // reference maximum of the row's scores, log2 domain (replicated per row)
   float l;  // this lane's partial sum of exp2(s - m) (summed across lanes at the end)
   f32x4 o[D / 16];
   __device__ void init() {
@@ -354,6 +417,23 @@ struct RowState {
     for (int c = 0; c < D / 16; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 };
+
+// The exponent base of a row. Online softmax only needs o and l to be taken
+// against one common reference m; the result sum(p v) / sum(p) does not
+// depend on it as long as nothing overflows. So m moves only when a block's
+// maximum exceeds it by more than kRescaleLog2: then p = exp2(s - m) stays at
+// most 2^kRescaleLog2 (fine for fp32 sums and for bf16/fp16 P operands) and
+// most blocks skip the rescale of o altogether. A row that has seen no key yet
+// (m = -inf, o = l = 0) takes the first block's maximum without a rescale.
+constexpr float kRescaleLog2 = 8.0f;
+// Updates m for a block whose row maximum is mx; returns the factor for o
+// and l (exactly 1 when m stays).
+__device__ inline float advance_max(float& m, float mx) {
+  const bool up = mx > m + kRescaleLog2;
+  const float alpha = (up && m != neg_inf()) ? fast_exp2(m - mx) : 1.0f;
+  m = up ? mx : m;
+  return alpha;
+}
 
 // Where one wave's KV blocks live.
 template <class Storage>
@@ -384,21 +464,64 @@ __device__ inline void consume_block(RowState<D>& st, const typename Ops<E, D>::
   float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   mx = max_xor16(mx);
   mx = max_xor32(mx);
-  const float m_new = fmaxf(st.m, mx);
-  const float m_use = m_new == neg_inf() ? 0.f : m_new;
-  // An unchanged maximum (including a row that has seen no key yet) keeps
-  // alpha exactly 1, so the rescale below is skipped when no row moved.
-  const float alpha = st.m == m_new ? 1.0f : fast_exp2(st.m - m_use);
+  const float alpha = advance_max(st.m, mx);
+  const float m_use = st.m == neg_inf() ? 0.f : st.m;
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - m_use);
   st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-  st.m = m_new;
   if (__any(alpha != 1.0f)) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) st.o[c] *= alpha;
   }
   O::pv(st.o, kv, O::pack_p(p));
+}
+
+// One block against RT row tiles that share it (prefill): every tile's
+// scores, then every tile's softmax update, one combined rescale test, and
+// the block's PV operand built once for all tiles. Straight-line code, so
+// the tiles' independent MFMA and VALU chains interleave.
+template <class E, int D, int RT>
+__device__ inline void consume_block_tiles(RowState<D> (&st)[RT], const typename Ops<E, D>::KV& kv,
+                                           const typename Ops<E, D>::Q (&q)[RT], int key0,
+                                           const int (&key_end)[RT], float scale_log2, int lane) {
+  using O = Ops<E, D>;
+  const int grp = lane >> 4;
+  f32x4 acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = O::scores(kv, q[t]);
+  typename O::P pk[RT];
+  float alpha[RT];
+  bool moved = false;
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = key0 + 4 * grp + i;
+      s[i] = key < key_end[t] ? acc[t][i] * scale_log2 : neg_inf();
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
+    alpha[t] = advance_max(st[t].m, mx);
+    moved = moved || alpha[t] != 1.0f;
+    const float m_use = st[t].m == neg_inf() ? 0.f : st[t].m;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - m_use);
+    st[t].l = st[t].l * alpha[t] + ((p[0] + p[1]) + (p[2] + p[3]));
+    pk[t] = O::pack_p(p);
+  }
+  if (__any(moved)) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) st[t].o[c] *= alpha[t];
+  }
+  const typename O::VA va = O::build_v(kv);
+#pragma unroll
+  for (int t = 0; t < RT; ++t) O::pv_with(st[t].o, va, pk[t]);
 }
 
 // Streams this wave's contiguous run of n blocks, starting at logical block

@@ -248,15 +248,23 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
   a.num_tokens = num_tokens;
   a.causal = causal;
   a.split_blocks = max_blocks_per_seq;
-  const int waves = 4;
-  const int tokens_per_tile = waves * (16 / a.group);
-  a.num_tiles = max_query_len * a.group <= 16
-                    ? 1
-                    : (max_query_len + tokens_per_tile - 1) / tokens_per_tile;
-  const int64_t grid = (int64_t)a.num_tiles * num_seqs * cache->num_kv_heads;
-  if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-  return launched(pa::launch_attention(a, cache->dtype, cache->head_dim, waves, grid,
-                                       static_cast<hipStream_t>(stream)));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // prefill chunks (query rows x group > 16): the LDS-staged prefill kernel
+  if ((int64_t)max_query_len * a.group > 16) {
+    const int tt = pa::prefill_tile_tokens(cache->dtype, a.group);
+    a.num_tiles = (max_query_len + tt - 1) / tt;
+    const int64_t pgrid = (int64_t)a.num_tiles * num_seqs * cache->num_kv_heads;
+    if (pgrid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    const pa_status ps = launched(pa::launch_prefill(a, cache->dtype, cache->head_dim, pgrid, st));
+    if (ps != PA_OK) return ps;
+  }
+  // single-tile requests (decode rows and short queries)
+  a.num_tiles = 1;
+  const int64_t grid = (int64_t)num_seqs * cache->num_kv_heads;
+  return launched(pa::launch_attention(a, cache->dtype, cache->head_dim,
+                                       decode_waves((max_seq_len + kSupportedBlock - 1) /
+                                                    kSupportedBlock),
+                                       grid, st));
 }
 
 size_t pa_decode_balanced_workspace_bytes(const pa_kv_cache* cache, int num_seqs,

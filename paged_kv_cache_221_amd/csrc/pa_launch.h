@@ -78,6 +78,10 @@ hipError_t launch_write_kv(const pa_kv_cache* cache, const void* k_new, const vo
 hipError_t launch_attention(const AttnArgs& args, pa_dtype dtype, int head_dim, int waves,
                             int64_t grid, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& args, pa_dtype out_dtype, hipStream_t stream);
+// Query tokens one prefill workgroup covers for GQA group size `group`.
+int prefill_tile_tokens(pa_dtype dtype, int group);
+hipError_t launch_prefill(const AttnArgs& args, pa_dtype dtype, int head_dim, int64_t grid,
+                          hipStream_t stream);
 // Resident waves of the balanced decode kernel on the current device (0 on error).
 int balanced_total_waves(pa_dtype dtype, int head_dim);
 hipError_t launch_balanced(const BalancedArgs& args, pa_dtype dtype, hipStream_t stream);

@@ -1,0 +1,217 @@
+// prefill.hip -- the chunked-prefill rows of a varlen step [P1 §07] on gfx950.
+//
+// A request whose query rows times the GQA group exceed one 16-row tile is a
+// prefill chunk: query row i of it sees keys 0 .. c + i (its cached context c
+// plus itself and earlier new tokens [P1 §04 causal mask]). Prefill is a dense
+// contraction [P1 §04 table: GEMM, compute-bound], so the work is arranged for
+// operand reuse: a workgroup owns 4 waves x RT row tiles x 16/g query tokens
+// of one (request, KV head); every KV block is fetched once per workgroup into
+// double-buffered LDS through a register prefetch ring of PA_PREFILL_RING
+// blocks, and each wave reads the block's MFMA operands from LDS once and
+// applies them to all of its RT row tiles. Scores and probabilities stay in
+// registers (the FlashAttention principle [P3 §3.4]).
+#include "attn_tile.h"
+#include "pa_launch.h"
+
+#ifndef PA_PREFILL_RT
+#define PA_PREFILL_RT 2
+#endif
+#ifndef PA_PREFILL_RING
+#define PA_PREFILL_RING 4
+#endif
+#ifndef PA_PREFILL_OCC
+#define PA_PREFILL_OCC 2
+#endif
+
+namespace pa {
+namespace {
+
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillThreads = kPrefillWaves * kWave;
+static_assert(PA_PREFILL_RING % 4 == 0, "the ring (halved for fp32) alternates two LDS buffers");
+
+// How one workgroup stages a block's head slice (16 keys) in LDS.
+template <class E, int D>
+struct Stage {
+  using S = typename Ops<E, D>::storage;
+  static constexpr int kRowBytes = D * (int)sizeof(S);      // one key's slice
+  static constexpr int kLdsRow = kRowBytes + 16;            // padded: no bank conflicts
+  static constexpr int kChunksPerRow = kRowBytes / 16;
+  static constexpr int kChunks = kBlockTokens * kChunksPerRow;
+  static constexpr int kPerThread = (kChunks + kPrefillThreads - 1) / kPrefillThreads;
+  struct Regs {
+    u32x4 k[kPerThread];
+    u32x4 v[kPerThread];
+  };
+};
+
+template <class E, int D, int RT, int RING>
+__global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kernel(const AttnArgs a) {
+  using O = Ops<E, D>;
+  using S = typename O::storage;
+  using St = Stage<E, D>;
+  __shared__ __attribute__((aligned(16))) char s_k[2][kBlockTokens * St::kLdsRow];
+  __shared__ __attribute__((aligned(16))) char s_v[2][kBlockTokens * St::kLdsRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  // tiles in descending order: the tiles that see the most keys start first
+  int u = blockIdx.x;
+  const int kvh = u % a.num_kv_heads;
+  u /= a.num_kv_heads;
+  const int r = u % a.num_seqs;
+  const int tile = a.num_tiles - 1 - u / a.num_seqs;
+
+  int lo = a.cu_seqlens[r], hi = a.cu_seqlens[r + 1];
+  lo = min(max(lo, 0), a.num_tokens);
+  hi = min(max(hi, lo), a.num_tokens);
+  const int q_lo = lo, n = hi - lo;
+  const int g = a.group;
+  if (n * g <= 16) return;  // a single-tile request: handled by the decode kernel
+  const int seq_len = min(max(a.seq_lens[r], 0), a.max_blocks * kBlockTokens);
+  const int ctx = max(seq_len - n, 0);
+  const int tpw = 16 / g;                               // tokens per row tile
+  const int tile_tokens = kPrefillWaves * RT * tpw;
+  const int tok_base = tile * tile_tokens;
+  if (tok_base >= n) return;
+  const int tile_end = min(tok_base + tile_tokens, n);
+  const int kmax = a.causal ? min(ctx + tile_end, seq_len) : seq_len;
+  const int nblk = (kmax + kBlockTokens - 1) / kBlockTokens;
+  if (nblk <= 0) return;
+
+  // this wave's row tiles
+  const int row = lane & 15, grp = lane >> 4;
+  typename O::Q q[RT];
+  RowState<D> st[RT];
+  int key_end[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int tok0 = tok_base + (wave * RT + rt) * tpw;
+    const int tok = tok0 + row / g, hh = row - (row / g) * g;
+    const bool valid = row < tpw * g && tok < n;
+    key_end[rt] = !valid ? 0 : (a.causal ? min(ctx + tok + 1, seq_len) : seq_len);
+    const S* qrow = static_cast<const S*>(a.q) +
+                    ((int64_t)(q_lo + (valid ? tok : 0)) * a.num_heads + kvh * g + hh) * D;
+    O::load_q(q[rt], qrow, valid, lane);
+    st[rt].init();
+  }
+
+  // staging of KV blocks: HBM -> registers (ring) -> LDS (two buffers)
+  const int64_t rs = (int64_t)a.num_kv_heads * D;
+  const int64_t block_elems = (int64_t)kBlockTokens * rs;
+  const int row_bytes_g = (int)(rs * (int64_t)sizeof(S));
+  const S* k_head = static_cast<const S*>(a.k_cache) + (int64_t)kvh * D;
+  const S* v_head = static_cast<const S*>(a.v_cache) + (int64_t)kvh * D;
+  const __attribute__((address_space(4))) int32_t* tab =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)r * a.max_blocks);
+  auto issue = [&](typename St::Regs& rg, int i) {
+    const int pb = tab[min(i, nblk - 1)];
+    const bool ok = i < nblk && pb >= 0 && pb < a.num_blocks;
+    const int keys = min(seq_len - i * kBlockTokens, kBlockTokens);
+    const int range = ok ? keys * row_bytes_g : 0;
+    const int64_t base = (int64_t)(ok ? pb : 0) * block_elems;
+    const Rsrc rk = make_rsrc(k_head + base, range), rv = make_rsrc(v_head + base, range);
+#pragma unroll
+    for (int p = 0; p < St::kPerThread; ++p) {
+      const int c = tid + p * kPrefillThreads;
+      // a thread without a chunk reads past the range: zeros, no memory access
+      const int off = c < St::kChunks
+                          ? (c / St::kChunksPerRow) * row_bytes_g + (c % St::kChunksPerRow) * 16
+                          : 0x7ffffff0;
+      rg.k[p] = buf_load16(rk, off);
+      rg.v[p] = buf_load16(rv, off);
+    }
+  };
+  auto stage = [&](const typename St::Regs& rg, int buf) {
+#pragma unroll
+    for (int p = 0; p < St::kPerThread; ++p) {
+      const int c = tid + p * kPrefillThreads;
+      if (c < St::kChunks) {
+        const int off = (c / St::kChunksPerRow) * St::kLdsRow + (c % St::kChunksPerRow) * 16;
+        *reinterpret_cast<u32x4*>(&s_k[buf][off]) = rg.k[p];
+        *reinterpret_cast<u32x4*>(&s_v[buf][off]) = rg.v[p];
+      }
+    }
+  };
+
+  typename St::Regs ring[RING];
+#pragma unroll
+  for (int j = 0; j < RING; ++j) issue(ring[j], j);
+  for (int i0 = 0; i0 < nblk; i0 += RING) {
+#pragma unroll
+    for (int j = 0; j < RING; ++j) {
+      const int i = i0 + j;
+      const int buf = j & 1;
+      stage(ring[j], buf);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ring[j], i + RING);
+      __builtin_amdgcn_sched_barrier(0);
+      // Unconditional, like the loads: a padding block past nblk was read as
+      // zeros and is fully masked (every key_end is at most nblk * 16), so it
+      // adds nothing, and the accumulators stay in one set of registers.
+      typename O::KV kv;
+      O::load_lds(kv, s_k[buf], s_v[buf], St::kLdsRow, lane);
+      consume_block_tiles<E, D, RT>(st, kv, q, i * kBlockTokens, key_end, a.scale_log2, lane);
+    }
+  }
+
+  // epilogue: normalise and store every valid row
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    st[rt].l = sum_xor16(st[rt].l);
+    st[rt].l = sum_xor32(st[rt].l);
+    const int tok0 = tok_base + (wave * RT + rt) * tpw;
+    const int tok = tok0 + row / g, hh = row - (row / g) * g;
+    if (row < tpw * g && tok < n) {
+      const float inv = st[rt].l > 0.f ? 1.f / st[rt].l : 0.f;
+      S* dst = static_cast<S*>(a.out) +
+               ((int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh) * D + (D / 4) * grp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v[D / 16];
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) v[c] = st[rt].o[c][i] * inv;
+        store_chunk<E, D>(dst + (D / 16) * i, v);
+      }
+    }
+  }
+}
+
+// fp32 operands are twice the size: half the row tiles and half the ring.
+template <class E>
+constexpr int prefill_rt() {
+  return sizeof(typename E::storage) == 4 ? PA_PREFILL_RT / 2 : PA_PREFILL_RT;
+}
+template <class E>
+constexpr int prefill_ring() {
+  return sizeof(typename E::storage) == 4 ? PA_PREFILL_RING / 2 : PA_PREFILL_RING;
+}
+
+template <class E, int D>
+hipError_t launch_pf(const AttnArgs& a, int64_t grid, hipStream_t stream) {
+  prefill_kernel<E, D, prefill_rt<E>(), prefill_ring<E>()>
+      <<<dim3((unsigned)grid), dim3(kPrefillThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_tile_tokens(pa_dtype dtype, int group) {
+  const int rt = dtype == PA_F32 ? prefill_rt<F32>() : prefill_rt<Bf16>();
+  return kPrefillWaves * rt * (16 / group);
+}
+
+hipError_t launch_prefill(const AttnArgs& a, pa_dtype dtype, int head_dim, int64_t grid,
+                          hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  switch (dtype) {
+    case PA_BF16: return head_dim == 128 ? launch_pf<Bf16, 128>(a, grid, stream) : launch_pf<Bf16, 64>(a, grid, stream);
+    case PA_F16: return head_dim == 128 ? launch_pf<F16, 128>(a, grid, stream) : launch_pf<F16, 64>(a, grid, stream);
+    case PA_F32: return head_dim == 128 ? launch_pf<F32, 128>(a, grid, stream) : launch_pf<F32, 64>(a, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -289,3 +289,23 @@ def test_binding_rejects_bad_arguments(gpu_lib):
         # max_seq_len larger than the table can hold
         pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
                      10 ** 6, lay.scale)
+
+
+@pytest.mark.parametrize("case", [("bf16", 128, 32, 8), ("f16", 128, 8, 8), ("bf16", 64, 16, 2),
+                                  ("f32", 128, 8, 2)], ids=lambda c: "-".join(map(str, c)))
+def test_varlen_long_prefill_tiles(gpu_lib, case):
+    """Prefill chunks spanning several workgroup tiles with ragged ends, next to
+    decode rows."""
+    dtype, d, hq, hkv = case
+    lay = small_varlen(400 + hq, dtype=dtype, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       prefill=((300, 100), (129, 0), (65, 700)), decode_lens=(5, 333))
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    want, _ = varlen_oracle(st, snap, req)
+    err = max_err(gpu_rows(out, dtype), want)
+    print(f"{lay.name}: long prefill max|err| = {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
