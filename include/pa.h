@@ -135,14 +135,16 @@ pa_status pa_lse_merge(void *out, float *lse_out, const float *o_part,
                        pa_dtype out_dtype, void *stream);
 
 /* Balanced paged decode [P1 §04; P1 §07]: the same result as pa_decode, for
- * batches of ragged lengths. The batch's work -- every (request, KV head,
- * 16-token block) in request-major order -- is cut into one equal contiguous
- * share per wave the GPU can hold at once, so short requests do not leave the
- * GPU idle while the longest ones finish. A share's end that cuts a
- * (request, KV head) is written as a partial (softmax-normalised output and
- * log-sum-exp) and a second kernel renormalises the partials, as the
- * Flash-Decoding merge of [P1 §07] does, with split points chosen for
- * balance. Two kernels are launched on `stream`.
+ * batches of ragged lengths. The batch's work -- every (request, group of KV
+ * heads, 16-token block) in request-major order -- is cut into one equal
+ * contiguous share per workgroup the GPU can hold at once, so short requests
+ * do not leave the GPU idle while the longest ones finish; the waves of a
+ * workgroup (one per KV head of the group) read each block together. A
+ * share's end that cuts a (request, KV head) is written as a partial
+ * (softmax-normalised output and log-sum-exp) and a second kernel
+ * renormalises the partials, as the Flash-Decoding merge of [P1 §07] does,
+ * with split points chosen for balance. Two kernels are launched on
+ * `stream`.
  *   workspace       : caller-owned device memory of at least
  *                     pa_decode_balanced_workspace_bytes(...) bytes; its
  *                     contents need not be initialised; two calls in flight

@@ -68,8 +68,17 @@ __device__ inline float sum_xor32(float v) {
 // byte range (reads at or past it return zeros), gfx9 data-format word.
 using Rsrc = __amdgpu_buffer_rsrc_t;
 constexpr int kRsrcFlags = 0x00020000;
+// `base` and `range_bytes` must be the same in every lane of the wave (one
+// block of one head). Reading them from the first lane puts the resource in
+// scalar registers even where the compiler cannot prove that (64-bit index
+// math done on the vector unit): a resource in vector registers makes it
+// guard every load with a loop over the distinct values in the wave.
 __device__ inline Rsrc make_rsrc(const void* base, int range_bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, range_bytes,
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(range_bytes),
                                           kRsrcFlags);
 }
 __device__ inline u32x4 buf_load16(Rsrc r, int off) {
@@ -533,7 +542,11 @@ __device__ inline void consume_block_tiles(RowState<D> (&st)[RT], const typename
 // touching memory. Every iteration loads and consumes unconditionally (a
 // padding block is consumed with no visible key), which lets the compiler wait
 // for exactly the block it consumes instead of draining every load.
-template <class E, int D, int DEPTH>
+//
+// With SYNC, the workgroup meets at a barrier once per DEPTH blocks, so that
+// waves walking the same blocks (other heads) keep fetching them together;
+// every wave of the workgroup must then run the same number of blocks.
+template <class E, int D, int DEPTH, bool SYNC = false>
 __device__ inline void stream_blocks(RowState<D>& st, const typename Ops<E, D>::Q& q,
                                      const KvView<typename Ops<E, D>::storage>& kv_view,
                                      int b_begin, int n, int key_end, int seq_len,
@@ -565,6 +578,7 @@ __device__ inline void stream_blocks(RowState<D>& st, const typename Ops<E, D>::
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) load(buf[j], j);
   for (int i0 = 0; i0 < n; i0 += DEPTH) {
+    if constexpr (SYNC) __syncthreads();
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
       consume(buf[j], i0 + j);

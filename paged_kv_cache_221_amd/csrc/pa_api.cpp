@@ -72,26 +72,30 @@ int decode_waves(int blocks) {
   return 1;
 }
 
-// Resident waves of the balanced kernel, cached per (device, dtype, head_dim):
-// the value depends only on the compiled kernel and the device.
+// Resident waves of the balanced kernel, cached per (device, dtype, head_dim,
+// waves per workgroup): the value depends only on the compiled kernel and the
+// device.
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_total_waves[kMaxDevices][3][2];
+std::atomic<int> g_total_waves[kMaxDevices][3][2][4];
 struct TotalWavesInit {
   TotalWavesInit() {
     for (auto& d : g_total_waves)
       for (auto& t : d)
-        for (auto& v : t) v.store(-1);
+        for (auto& h : t)
+          for (auto& v : h) v.store(-1);
   }
 } g_total_waves_init;
 
-int total_waves(pa_dtype dtype, int head_dim) {
+int total_waves(pa_dtype dtype, int head_dim, int num_kv_heads) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev >= kMaxDevices) return pa::balanced_total_waves(dtype, head_dim);
-  std::atomic<int>& slot = g_total_waves[dev][(int)dtype][head_dim == 128 ? 1 : 0];
+  if (dev >= kMaxDevices) return pa::balanced_total_waves(dtype, head_dim, num_kv_heads);
+  const int nw = pa::balanced_group_waves(num_kv_heads);
+  const int nw_index = nw == 8 ? 3 : nw == 4 ? 2 : nw == 2 ? 1 : 0;
+  std::atomic<int>& slot = g_total_waves[dev][(int)dtype][head_dim == 128 ? 1 : 0][nw_index];
   int v = slot.load();
   if (v < 0) {
-    v = pa::balanced_total_waves(dtype, head_dim);
+    v = pa::balanced_total_waves(dtype, head_dim, num_kv_heads);
     slot.store(v);
   }
   return v;
@@ -103,14 +107,15 @@ struct BalancedLayout {
   size_t records, part_o, part_lse, total;
 };
 
-// Piece slots: at most total_waves + (segments) of them, each `group` rows.
+// Workspace: one record per segment, then the partial outputs and LSEs of
+// every possible piece slot (`group` rows each).
 BalancedLayout balanced_layout(int tw, int group, int head_dim, int num_seqs,
                                int num_kv_heads) {
   const size_t segs = (size_t)num_seqs * num_kv_heads;
-  const size_t slots = (size_t)tw + segs;
+  const size_t slots = (size_t)pa::balanced_piece_slots(tw, (long long)segs);
   BalancedLayout l;
   l.records = 0;
-  l.part_o = align256(segs * 2 * sizeof(int32_t));
+  l.part_o = l.records + align256(segs * 2 * sizeof(int32_t));
   l.part_lse = l.part_o + align256(slots * group * head_dim * sizeof(float));
   l.total = l.part_lse + align256(slots * group * sizeof(float));
   return l;
@@ -273,7 +278,7 @@ size_t pa_decode_balanced_workspace_bytes(const pa_kv_cache* cache, int num_seqs
       num_heads % cache->num_kv_heads != 0)
     return 0;
   if (cache->head_dim != 64 && cache->head_dim != 128) return 0;
-  const int tw = total_waves(cache->dtype, cache->head_dim);
+  const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
   if (tw <= 0) return 0;
   return balanced_layout(tw, num_heads / cache->num_kv_heads, cache->head_dim, num_seqs,
                          cache->num_kv_heads)
@@ -292,7 +297,7 @@ pa_status pa_decode_balanced(const pa_kv_cache* cache, void* out, const void* q,
   if (num_seqs == 0) return PA_OK;
   if (out == nullptr || q == nullptr || block_table == nullptr || seq_lens == nullptr)
     return PA_ERR_NULL;
-  const int tw = total_waves(cache->dtype, cache->head_dim);
+  const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
   if (tw <= 0) return PA_ERR_LAUNCH;
   const int group = num_heads / cache->num_kv_heads;
   const BalancedLayout lay =

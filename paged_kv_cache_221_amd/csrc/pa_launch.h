@@ -49,6 +49,18 @@ struct MergeArgs {
 // Balanced decode: the batch's (request, KV head, block) items in equal
 // shares, one per resident wave.
 constexpr int kMaxBalancedSeqs = 4096;
+// Waves (KV heads) per workgroup of the balanced kernel: the largest of
+// 8, 4, 2, 1 that divides the KV head count.
+inline int balanced_group_waves(int num_kv_heads) {
+  for (int nw = 8; nw > 1; nw >>= 1)
+    if (num_kv_heads % nw == 0) return nw;
+  return 1;
+}
+// Partial-output slots: total_waves + B * Hkv of them (`group` rows each).
+inline long long balanced_piece_slots(int total_waves, long long segments) {
+  return (long long)total_waves + segments;
+}
+
 struct BalancedArgs {
   const void* k_cache;
   const void* v_cache;
@@ -56,8 +68,8 @@ struct BalancedArgs {
   void* out;                  // [B, Hq, D]
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* part_o;              // [total_waves + B*Hkv, group, D] partial outputs
-  float* part_lse;            // [total_waves + B*Hkv, group] partial LSEs (log2 domain)
+  float* part_o;              // [balanced_piece_slots, group, D] partial outputs
+  float* part_lse;            // [balanced_piece_slots, group] partial LSEs (log2 domain)
   int2* records;              // [B, Hkv] (first piece slot, piece count; 0 = no merge)
   int num_seqs;
   int num_heads;
@@ -82,8 +94,9 @@ hipError_t launch_lse_merge(const MergeArgs& args, pa_dtype out_dtype, hipStream
 int prefill_tile_tokens(pa_dtype dtype, int group);
 hipError_t launch_prefill(const AttnArgs& args, pa_dtype dtype, int head_dim, int64_t grid,
                           hipStream_t stream);
-// Resident waves of the balanced decode kernel on the current device (0 on error).
-int balanced_total_waves(pa_dtype dtype, int head_dim);
+// Resident waves of the balanced decode kernel on the current device for
+// this head count (0 on error).
+int balanced_total_waves(pa_dtype dtype, int head_dim, int num_kv_heads);
 hipError_t launch_balanced(const BalancedArgs& args, pa_dtype dtype, hipStream_t stream);
 
 }  // namespace pa
