@@ -232,8 +232,12 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
 }
 
 // One wave per (request, query head): renormalises the pieces of a segment
-// that was cut between waves. Lane j reads piece j's LSE; the outputs of all
-// pieces are then read with independent loads, lanes over head_dim.
+// that was cut between workgroups. The record gives where the pieces are;
+// then every piece's LSE (lane j reads piece j) and the outputs of the first
+// kMergeBatch pieces (lanes over head_dim) are loaded together, so a segment
+// of up to kMergeBatch pieces costs two dependent memory round trips; later
+// pieces are loaded kMergeBatch at a time.
+constexpr int kMergeBatch = 16;
 template <class E>
 __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const BalancedArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -245,25 +249,54 @@ __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const Balance
   const int D = a.head_dim;
   const int2 rec = a.records[(int64_t)r * a.num_kv_heads + kvh];
   const int np = rec.y;
-  if (np <= 0) return;  // written whole by one wave, or an empty request
+  if (np <= 0) return;  // written whole by one workgroup, or an empty request
+  const int d0 = lane, d1 = lane + kWave;
+  const float* lse = a.part_lse + (int64_t)rec.x * g + row;
+  const float* po = a.part_o + ((int64_t)rec.x * g + row) * D;
+  // issue the first batch of outputs together with the LSEs
+  float o0[kMergeBatch], o1[kMergeBatch];
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    const bool ok = k < np;
+    o0[k] = ok && d0 < D ? po[(int64_t)k * g * D + d0] : 0.f;
+    o1[k] = ok && d1 < D ? po[(int64_t)k * g * D + d1] : 0.f;
+  }
   float mx = neg_inf();
-  for (int j = lane; j < np; j += kWave) mx = fmaxf(mx, a.part_lse[((int64_t)rec.x + j) * g + row]);
+  for (int j = lane; j < np; j += kWave) mx = fmaxf(mx, lse[(int64_t)j * g]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, xor_shuffle(mx, m));
   const float mu = mx == neg_inf() ? 0.f : mx;
   float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
-  const int d0 = lane, d1 = lane + kWave;
   for (int c = 0; c < np; c += kWave) {
     const int j = c + lane;
-    const float w = j < np ? fast_exp2(a.part_lse[((int64_t)rec.x + j) * g + row] - mu) : 0.f;
+    const float w = j < np ? fast_exp2(lse[(int64_t)j * g] - mu) : 0.f;
     wsum += w;
     const int cnt = min(kWave, np - c);
-#pragma unroll 8
-    for (int k = 0; k < cnt; ++k) {
-      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
-      const float* src = a.part_o + (((int64_t)rec.x + c + k) * g + row) * D;
-      if (d0 < D) acc0 += wk * src[d0];
-      if (d1 < D) acc1 += wk * src[d1];
+    // pieces c + b0 .. c + b0 + kMergeBatch - 1: all loads first, then the sums
+    for (int b0 = 0; b0 < cnt; b0 += kMergeBatch) {
+      float x0[kMergeBatch], x1[kMergeBatch];
+      if (c == 0 && b0 == 0) {
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+          x0[k] = o0[k];
+          x1[k] = o1[k];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+          const bool ok = b0 + k < cnt;
+          const float* src = po + (int64_t)(c + b0 + k) * g * D;
+          x0[k] = ok && d0 < D ? src[d0] : 0.f;
+          x1[k] = ok && d1 < D ? src[d1] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        // b0 + k < kWave: b0 is a multiple of kMergeBatch below cnt <= kWave
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), b0 + k));
+        acc0 += wk * x0[k];  // zero past cnt (loaded as 0, weight 0)
+        acc1 += wk * x1[k];
+      }
     }
   }
 #pragma unroll
