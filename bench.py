@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged GQA decode: achieved HBM GB/s (% of peak) + decode tokens/s per layer"
 PEAK_HBM_GBS = 8000.0
-ATTN_SOURCES = ["attention.hip", "balanced.hip", "attn_tile.h", "pa_api.cpp"]
+ATTN_SOURCES = ["attention.hip", "balanced.hip", "attn_tile.h", "pa_launch.h", "pa_api.cpp"]
 
 
 def kernel_source_hash() -> str:
@@ -232,14 +232,17 @@ def secondary(args):
             nbytes = decode_bytes(lay)
         else:
             out = torch.empty_like(st.q)
+            ws = torch.empty(pa.pa_varlen_workspace_bytes(st.k_cache, st.v_cache, lay.num_seqs,
+                                                          lay.num_heads),
+                             dtype=torch.uint8, device="cuda")
 
-            def step(ev=None, st=st, lay=lay, out=out):
+            def step(ev=None, st=st, lay=lay, out=out, ws=ws):
                 pa.pa_write_kv(st.k_cache, st.v_cache, st.k_new, st.v_new, st.slot_mapping)
                 if ev is not None:
                     ev[0].record()
                 pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
                              st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
-                             out=out)
+                             out=out, workspace=ws)
                 if ev is not None:
                     ev[1].record()
             nbytes = varlen_bytes(lay)

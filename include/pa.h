@@ -166,15 +166,26 @@ pa_status pa_decode_balanced(const pa_kv_cache *cache, void *out, const void *q,
  * c_r = seq_len[r] - n_r. With causal != 0, row i of the request sees keys
  * 0 .. c_r + i (a query sees itself and earlier tokens); with causal == 0,
  * all seq_len[r] keys. Decode rows are the n_r == 1 case.
+ * Requests with n_r * group > 16 (prefill chunks) run in a tiled kernel;
+ * the others in the balanced kernel of pa_decode_balanced when a workspace is
+ * given (partials merged by a further kernel), else one workgroup per
+ * (request, KV head).
  *   out, q        : [T, Hq, D] in cache->dtype
  *   cu_seqlens_q  : int32 [B + 1], cu[0] = 0, non-decreasing, cu[B] = T
  *   seq_lens      : int32 [B]; KV length including this step's n_r tokens
- *   max_query_len, max_seq_len : host upper bounds (size the launch) */
+ *   max_query_len, max_seq_len : host upper bounds (size the launch)
+ *   workspace     : NULL, or caller-owned device memory of at least
+ *                   pa_varlen_workspace_bytes(...) bytes (contents need not
+ *                   be initialised; calls in flight at once must not share
+ *                   it); with more than 4096 requests it is not used
+ * Too small a non-NULL workspace returns PA_ERR_WORKSPACE. */
+size_t pa_varlen_workspace_bytes(const pa_kv_cache *cache, int num_seqs, int num_heads);
 pa_status pa_varlen(const pa_kv_cache *cache, void *out, const void *q,
                     const int32_t *cu_seqlens_q, const int32_t *seq_lens,
                     const int32_t *block_table, int num_seqs, int num_tokens,
                     int num_heads, int max_blocks_per_seq, int max_query_len,
-                    int max_seq_len, float scale, int causal, void *stream);
+                    int max_seq_len, float scale, int causal, void *workspace,
+                    size_t workspace_bytes, void *stream);
 
 /* Static English text for a status code. */
 const char *pa_status_str(pa_status status);

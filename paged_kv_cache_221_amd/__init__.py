@@ -17,5 +17,6 @@ from .api import (  # noqa: F401
     pa_splitk_num_splits,
     pa_status_str,
     pa_varlen,
+    pa_varlen_workspace_bytes,
     pa_write_kv,
 )

@@ -197,8 +197,18 @@ def pa_lse_merge(o_part, lse_part, seq_lens, max_seq_len: int, split_tokens: int
     return (out, lse_out) if lse_out is not None else out
 
 
+def pa_varlen_workspace_bytes(k_cache, v_cache, num_seqs: int, num_heads: int) -> int:
+    c = kv_cache_struct(k_cache, v_cache)
+    return int(_native.load().pa_varlen_workspace_bytes(ctypes.byref(c), int(num_seqs),
+                                                        int(num_heads)))
+
+
 def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_query_len: int,
-              max_seq_len: int, scale: float, causal: bool = True, out=None):
+              max_seq_len: int, scale: float, causal: bool = True, out=None, workspace="auto"):
+    """Varlen step. ``workspace``: "auto" allocates one of
+    ``pa_varlen_workspace_bytes`` bytes (the balanced path for single-tile
+    requests), None passes NULL (one workgroup per request and KV head), or a
+    uint8 GPU tensor."""
     lib = _native.load()
     c = kv_cache_struct(k_cache, v_cache)
     _dev(q, "q", k_cache.dtype)
@@ -213,8 +223,16 @@ def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_quer
     out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a uint8 GPU tensor')
+        need = pa_varlen_workspace_bytes(k_cache, v_cache, b, hq)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
     _check("pa_varlen", lib.pa_varlen(
         ctypes.byref(c), _ptr(out), _ptr(q), _ptr(cu_seqlens_q), _ptr(seq_lens),
         _ptr(block_table), b, t, hq, max_blocks, int(max_query_len), int(max_seq_len),
-        float(scale), 1 if causal else 0, _stream(q)))
+        float(scale), 1 if causal else 0, _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(q)))
     return out

@@ -86,6 +86,25 @@ struct Shares {
   __device__ int64_t range_of(int64_t x) const { return W >= T ? ((x + 1) * T - 1) / W : x; }
 };
 
+// Query rows [*lo, *lo + *n) of request i: one row (the request's own) for
+// decode, else from cu_seqlens (clamped to the batch like the other kernels).
+__device__ inline void request_rows(const BalancedArgs& a, int i, int* lo, int* n) {
+  if (a.cu_seqlens == nullptr) {
+    *lo = i;
+    *n = 1;
+    return;
+  }
+  int l = a.cu_seqlens[i], h = a.cu_seqlens[i + 1];
+  l = min(max(l, 0), a.num_tokens);
+  h = min(max(h, l), a.num_tokens);
+  *lo = l;
+  *n = h - l;
+}
+
+// Requests whose query rows (tokens x group) fill at most one 16-row tile
+// are this kernel's work; longer ones (prefill chunks) are another kernel's.
+__device__ inline bool single_tile(int n, int g) { return n >= 1 && n * g <= kTileRows; }
+
 // Slot of range j's piece of head-group segment sg, for one head. Ranges and
 // segments both advance with the item index, so j + sg differs for every
 // non-empty piece and the pieces of one segment sit at consecutive slots;
@@ -111,8 +130,10 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
   const int c0 = min(tid * per, B), c1 = min(c0 + per, B);
   int chunk = 0;
   for (int i = c0; i < c1; ++i) {
+    int q_lo, n;
+    request_rows(a, i, &q_lo, &n);
     const int len = min(max(a.seq_lens[i], 0), max_len);
-    const int nb = (len + kBlockTokens - 1) / kBlockTokens;
+    const int nb = single_tile(n, a.group) ? (len + kBlockTokens - 1) / kBlockTokens : 0;
     s_prefix[i + 1] = nb;
     chunk += nb;
   }
@@ -126,11 +147,15 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
   if (tid == 0) s_prefix[0] = 0;
   __syncthreads();
   if (blockIdx.x == 0) {
-    // requests with no KV have no work items: zero output, nothing to merge
+    // single-tile requests with no KV have no work items: zero output rows,
+    // nothing to merge (prefill requests' rows belong to the prefill kernel)
     for (int i = tid; i < B; i += T) {
       if (s_prefix[i + 1] != s_prefix[i]) continue;
-      S* dst = static_cast<S*>(a.out) + (int64_t)i * a.num_heads * D;
-      for (int e = 0; e < a.num_heads * D; ++e) dst[e] = S(0);
+      int q_lo, n;
+      request_rows(a, i, &q_lo, &n);
+      if (!single_tile(n, a.group)) continue;
+      S* dst = static_cast<S*>(a.out) + (int64_t)q_lo * a.num_heads * D;
+      for (int64_t e = 0; e < (int64_t)n * a.num_heads * D; ++e) dst[e] = S(0);
       for (int k = 0; k < a.num_kv_heads; ++k) a.records[(int64_t)i * a.num_kv_heads + k] = int2{0, 0};
     }
   }
@@ -157,7 +182,7 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
   int r = r_lo;
 
   const int row = lane & 15, grp = lane >> 4;
-  const bool row_valid = row < g;
+  const int tok = row / g, hh = row - tok * g;  // this lane's query token and head in group
   int64_t x = lo;
   while (x < hi) {
     while (r < B - 1 && (int64_t)HG * prefix(r + 1) <= x) ++r;
@@ -169,6 +194,14 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     const int b = __builtin_amdgcn_readfirstlane(off - hg * nb);
     const int len = __builtin_amdgcn_readfirstlane((int)min((int64_t)(nb - b), hi - x));
     const int seq_len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[r], 0), max_len));
+    int q_lo, n_r;
+    request_rows(a, r, &q_lo, &n_r);
+    q_lo = __builtin_amdgcn_readfirstlane(q_lo);
+    n_r = __builtin_amdgcn_readfirstlane(n_r);
+    const int ctx = max(seq_len - n_r, 0);
+    const bool row_valid = tok < n_r;
+    // bottom-right causal mask: token i of the request sees keys 0 .. ctx + i
+    const int key_end = !row_valid ? 0 : (a.causal ? min(ctx + tok + 1, seq_len) : seq_len);
     const int kvh = hg * NW + wave;
 
     KvView<S> view;
@@ -178,16 +211,15 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     view.table = a.block_table + (int64_t)r * a.max_blocks;
     view.num_blocks = a.num_blocks;
 
-    const int head = kvh * g + (row_valid ? row : 0);
+    const int head = kvh * g + (row_valid ? hh : 0);
+    const int64_t qrow = (int64_t)q_lo + (row_valid ? tok : 0);
     typename O::Q qop;
-    O::load_q(qop, static_cast<const S*>(a.q) + ((int64_t)r * a.num_heads + head) * D, row_valid,
-              lane);
+    O::load_q(qop, static_cast<const S*>(a.q) + (qrow * a.num_heads + head) * D, row_valid, lane);
     RowState<D> st;
     st.init();
     // every wave of the workgroup walks the same blocks: same trip count
-    stream_blocks<E, D, bal_depth<E>(), PA_BAL_SYNC != 0>(st, qop, view, b, len,
-                                                         row_valid ? seq_len : 0, seq_len,
-                                                         a.scale_log2, lane);
+    stream_blocks<E, D, bal_depth<E>(), PA_BAL_SYNC != 0>(st, qop, view, b, len, key_end,
+                                                         seq_len, a.scale_log2, lane);
     st.l = sum_xor16(st.l);
     st.l = sum_xor32(st.l);
 
@@ -196,7 +228,7 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     if (row_valid) {
       const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
       if (whole) {
-        S* dst = static_cast<S*>(a.out) + ((int64_t)r * a.num_heads + head) * D + (D / 4) * grp;
+        S* dst = static_cast<S*>(a.out) + (qrow * a.num_heads + head) * D + (D / 4) * grp;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v[D / 16];
@@ -205,7 +237,7 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
           store_chunk<E, D>(dst + (D / 16) * i, v);
         }
       } else {
-        const int64_t slot = ((int64_t)wave * head_slots + piece_slot(j, sg)) * g + row;
+        const int64_t slot = ((int64_t)wave * head_slots + piece_slot(j, sg)) * a.slot_rows + row;
         float* dst = a.part_o + slot * D + (D / 4) * grp;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -231,7 +263,7 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
   }
 }
 
-// One wave per (request, query head): renormalises the pieces of a segment
+// One wave per (request, query head, query token): renormalises the pieces of a segment
 // that was cut between workgroups. The record gives where the pieces are;
 // then every piece's LSE (lane j reads piece j) and the outputs of the first
 // kMergeBatch pieces (lanes over head_dim) are loaded together, so a segment
@@ -241,35 +273,43 @@ constexpr int kMergeBatch = 16;
 template <class E>
 __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const BalancedArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int toks = a.slot_rows / a.group;  // query tokens a slot holds
   const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  if (unit >= (int64_t)a.num_seqs * a.num_heads) return;
-  const int r = (int)(unit / a.num_heads);
-  const int h = (int)(unit - (int64_t)r * a.num_heads);
-  const int g = a.group, kvh = h / g, row = h - kvh * g;
+  if (unit >= (int64_t)a.num_seqs * a.num_heads * toks) return;
+  const int tok = (int)(unit % toks);
+  const int64_t rh = unit / toks;
+  const int r = (int)(rh / a.num_heads);
+  const int h = (int)(rh - (int64_t)r * a.num_heads);
+  const int g = a.group, kvh = h / g;
+  int q_lo, n_r;
+  request_rows(a, r, &q_lo, &n_r);
+  if (!single_tile(n_r, g) || tok >= n_r) return;
   const int D = a.head_dim;
   const int2 rec = a.records[(int64_t)r * a.num_kv_heads + kvh];
   const int np = rec.y;
   if (np <= 0) return;  // written whole by one workgroup, or an empty request
   const int d0 = lane, d1 = lane + kWave;
-  const float* lse = a.part_lse + (int64_t)rec.x * g + row;
-  const float* po = a.part_o + ((int64_t)rec.x * g + row) * D;
+  const int64_t sr = a.slot_rows;
+  const int srow = tok * g + (h - kvh * g);  // row within the slot
+  const float* lse = a.part_lse + (int64_t)rec.x * sr + srow;
+  const float* po = a.part_o + ((int64_t)rec.x * sr + srow) * D;
   // issue the first batch of outputs together with the LSEs
   float o0[kMergeBatch], o1[kMergeBatch];
 #pragma unroll
   for (int k = 0; k < kMergeBatch; ++k) {
     const bool ok = k < np;
-    o0[k] = ok && d0 < D ? po[(int64_t)k * g * D + d0] : 0.f;
-    o1[k] = ok && d1 < D ? po[(int64_t)k * g * D + d1] : 0.f;
+    o0[k] = ok && d0 < D ? po[(int64_t)k * sr * D + d0] : 0.f;
+    o1[k] = ok && d1 < D ? po[(int64_t)k * sr * D + d1] : 0.f;
   }
   float mx = neg_inf();
-  for (int j = lane; j < np; j += kWave) mx = fmaxf(mx, lse[(int64_t)j * g]);
+  for (int j = lane; j < np; j += kWave) mx = fmaxf(mx, lse[(int64_t)j * sr]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, xor_shuffle(mx, m));
   const float mu = mx == neg_inf() ? 0.f : mx;
   float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
   for (int c = 0; c < np; c += kWave) {
     const int j = c + lane;
-    const float w = j < np ? fast_exp2(lse[(int64_t)j * g] - mu) : 0.f;
+    const float w = j < np ? fast_exp2(lse[(int64_t)j * sr] - mu) : 0.f;
     wsum += w;
     const int cnt = min(kWave, np - c);
     // pieces c + b0 .. c + b0 + kMergeBatch - 1: all loads first, then the sums
@@ -285,7 +325,7 @@ __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const Balance
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) {
           const bool ok = b0 + k < cnt;
-          const float* src = po + (int64_t)(c + b0 + k) * g * D;
+          const float* src = po + (int64_t)(c + b0 + k) * sr * D;
           x0[k] = ok && d0 < D ? src[d0] : 0.f;
           x1[k] = ok && d1 < D ? src[d1] : 0.f;
         }
@@ -303,7 +343,7 @@ __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const Balance
   for (int m = 32; m >= 1; m >>= 1) wsum += xor_shuffle(wsum, m);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   using S = typename E::storage;
-  S* out = static_cast<S*>(a.out) + unit * D;
+  S* out = static_cast<S*>(a.out) + (((int64_t)q_lo + tok) * a.num_heads + h) * D;
   if constexpr (sizeof(S) == 2) {
     if (d0 < D) out[d0] = E::from_float(acc0 * inv);
     if (d1 < D) out[d1] = E::from_float(acc1 * inv);
@@ -319,7 +359,7 @@ hipError_t launch_bal(const BalancedArgs& a, hipStream_t stream) {
       <<<dim3((unsigned)(a.total_waves / NW)), dim3(NW * kWave), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t units = (int64_t)a.num_seqs * a.num_heads;
+  const int64_t units = (int64_t)a.num_seqs * a.num_heads * (a.slot_rows / a.group);
   balanced_merge_kernel<E><<<dim3((unsigned)((units + 3) / 4)), dim3(4 * kWave), 0, stream>>>(a);
   return hipGetLastError();
 }

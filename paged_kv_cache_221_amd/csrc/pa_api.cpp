@@ -108,18 +108,22 @@ struct BalancedLayout {
 };
 
 // Workspace: one record per segment, then the partial outputs and LSEs of
-// every possible piece slot (`group` rows each).
-BalancedLayout balanced_layout(int tw, int group, int head_dim, int num_seqs,
+// every possible piece slot (`slot_rows` query rows each).
+BalancedLayout balanced_layout(int tw, int slot_rows, int head_dim, int num_seqs,
                                int num_kv_heads) {
   const size_t segs = (size_t)num_seqs * num_kv_heads;
   const size_t slots = (size_t)pa::balanced_piece_slots(tw, (long long)segs);
   BalancedLayout l;
   l.records = 0;
   l.part_o = l.records + align256(segs * 2 * sizeof(int32_t));
-  l.part_lse = l.part_o + align256(slots * group * head_dim * sizeof(float));
-  l.total = l.part_lse + align256(slots * group * sizeof(float));
+  l.part_lse = l.part_o + align256(slots * slot_rows * head_dim * sizeof(float));
+  l.total = l.part_lse + align256(slots * slot_rows * sizeof(float));
   return l;
 }
+
+// Rows per partial slot of the balanced kernel on a varlen batch: every
+// request that fits one 16-row tile, whatever max_query_len says.
+int varlen_slot_rows(int group) { return (pa::kTileRows / group) * group; }
 
 }  // namespace
 
@@ -231,11 +235,25 @@ pa_status pa_lse_merge(void* out, float* lse_out, const float* o_part, const flo
   return launched(pa::launch_lse_merge(a, out_dtype, static_cast<hipStream_t>(stream)));
 }
 
+size_t pa_varlen_workspace_bytes(const pa_kv_cache* cache, int num_seqs, int num_heads) {
+  if (check_cache(cache) != PA_OK || num_seqs < 0 || num_heads <= 0 ||
+      num_heads % cache->num_kv_heads != 0)
+    return 0;
+  if (cache->head_dim != 64 && cache->head_dim != 128) return 0;
+  const int group = num_heads / cache->num_kv_heads;
+  if (group > pa::kTileRows) return 0;
+  const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
+  if (tw <= 0) return 0;
+  return balanced_layout(tw, varlen_slot_rows(group), cache->head_dim, num_seqs,
+                         cache->num_kv_heads)
+      .total;
+}
+
 pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
                     const int32_t* cu_seqlens_q, const int32_t* seq_lens,
                     const int32_t* block_table, int num_seqs, int num_tokens, int num_heads,
                     int max_blocks_per_seq, int max_query_len, int max_seq_len, float scale,
-                    int causal, void* stream) {
+                    int causal, void* workspace, size_t workspace_bytes, void* stream) {
   pa_status s = check_cache(cache);
   if (s != PA_OK) return s;
   s = check_attention_shape(cache, num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale);
@@ -264,6 +282,40 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
     if (ps != PA_OK) return ps;
   }
   // single-tile requests (decode rows and short queries)
+  if (workspace != nullptr && num_seqs <= pa::kMaxBalancedSeqs) {
+    // balanced over the whole batch's KV, head groups read together
+    const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
+    if (tw <= 0) return PA_ERR_LAUNCH;
+    const int slot_rows = varlen_slot_rows(a.group);
+    const BalancedLayout lay =
+        balanced_layout(tw, slot_rows, cache->head_dim, num_seqs, cache->num_kv_heads);
+    if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    pa::BalancedArgs b{};
+    b.k_cache = cache->k_cache;
+    b.v_cache = cache->v_cache;
+    b.q = q;
+    b.out = out;
+    b.block_table = block_table;
+    b.seq_lens = seq_lens;
+    b.cu_seqlens = cu_seqlens_q;
+    b.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+    b.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
+    b.records = reinterpret_cast<int2*>(ws + lay.records);
+    b.num_tokens = num_tokens;
+    b.causal = causal;
+    b.slot_rows = slot_rows;
+    b.num_seqs = num_seqs;
+    b.num_heads = num_heads;
+    b.num_kv_heads = cache->num_kv_heads;
+    b.group = a.group;
+    b.head_dim = cache->head_dim;
+    b.num_blocks = cache->num_blocks;
+    b.max_blocks = max_blocks_per_seq;
+    b.total_waves = tw;
+    b.scale_log2 = a.scale_log2;
+    return launched(pa::launch_balanced(b, cache->dtype, st));
+  }
   a.num_tiles = 1;
   const int64_t grid = (int64_t)num_seqs * cache->num_kv_heads;
   return launched(pa::launch_attention(a, cache->dtype, cache->head_dim,
@@ -303,6 +355,7 @@ pa_status pa_decode_balanced(const pa_kv_cache* cache, void* out, const void* q,
   const BalancedLayout lay =
       balanced_layout(tw, group, cache->head_dim, num_seqs, cache->num_kv_heads);
   if (workspace == nullptr) return PA_ERR_NULL;
+  if (group > pa::kTileRows) return PA_ERR_UNSUPPORTED;
   if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   pa::BalancedArgs a{};
@@ -315,6 +368,10 @@ pa_status pa_decode_balanced(const pa_kv_cache* cache, void* out, const void* q,
   a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
   a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
   a.records = reinterpret_cast<int2*>(ws + lay.records);
+  a.cu_seqlens = nullptr;
+  a.num_tokens = num_seqs;
+  a.causal = 0;
+  a.slot_rows = group;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = cache->num_kv_heads;

@@ -48,11 +48,16 @@ struct MergeArgs {
 
 // Balanced decode: the batch's (request, KV head, block) items in equal
 // shares, one per resident wave.
+// Query rows of one MFMA row tile (tokens x GQA group).
+constexpr int kTileRows = 16;
 constexpr int kMaxBalancedSeqs = 4096;
 // Waves (KV heads) per workgroup of the balanced kernel: the largest of
 // 8, 4, 2, 1 that divides the KV head count.
+#ifndef PA_BAL_MAX_NW
+#define PA_BAL_MAX_NW 8
+#endif
 inline int balanced_group_waves(int num_kv_heads) {
-  for (int nw = 8; nw > 1; nw >>= 1)
+  for (int nw = PA_BAL_MAX_NW; nw > 1; nw >>= 1)
     if (num_kv_heads % nw == 0) return nw;
   return 1;
 }
@@ -64,13 +69,17 @@ inline long long balanced_piece_slots(int total_waves, long long segments) {
 struct BalancedArgs {
   const void* k_cache;
   const void* v_cache;
-  const void* q;              // [B, Hq, D]
-  void* out;                  // [B, Hq, D]
+  const void* q;              // [B, Hq, D], or [T, Hq, D] with cu_seqlens
+  void* out;                  // like q
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* part_o;              // [balanced_piece_slots, group, D] partial outputs
-  float* part_lse;            // [balanced_piece_slots, group] partial LSEs (log2 domain)
+  const int32_t* cu_seqlens;  // nullptr: one query token per request (decode)
+  float* part_o;              // [balanced_piece_slots, slot_rows, D] partial outputs
+  float* part_lse;            // [balanced_piece_slots, slot_rows] partial LSEs (log2 domain)
   int2* records;              // [B, Hkv] (first piece slot, piece count; 0 = no merge)
+  int num_tokens;             // T (rows of q) when cu_seqlens is set
+  int causal;                 // bottom-right causal mask within a request's rows
+  int slot_rows;              // rows per partial slot: group, or 16 / group * group
   int num_seqs;
   int num_heads;
   int num_kv_heads;

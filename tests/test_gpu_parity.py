@@ -219,8 +219,12 @@ VARLEN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["balanced", "direct"])
 @pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_varlen_parity(gpu_lib, case):
+def test_varlen_parity(gpu_lib, case, path):
+    """Prefill chunks, short multi-token queries (one tile) and decode rows;
+    single-tile requests through the balanced kernel (workspace given) or one
+    workgroup per (request, KV head) (no workspace)."""
     dtype, d, hq, hkv, causal = case
     lay = small_varlen(200 + d + hq, dtype=dtype, num_heads=hq, num_kv_heads=hkv, head_dim=d,
                        prefill=((40, 0), (70, 33), (17, 130), (3, 60), (2, 0)),
@@ -232,12 +236,41 @@ def test_varlen_parity(gpu_lib, case):
     check_cache_after_write(st, snap)
     out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
                        st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
-                       causal=causal)
+                       causal=causal, workspace="auto" if path == "balanced" else None)
     torch.cuda.synchronize()
     want, _ = varlen_oracle(st, snap, req, causal=causal)
     err = max_err(gpu_rows(out, lay.dtype), want)
-    print(f"{lay.name} causal={causal}: varlen max|err| = {err:.3e}", flush=True)
+    print(f"{lay.name} causal={causal} {path}: varlen max|err| = {err:.3e}", flush=True)
     assert err <= TOL[dtype]
+
+
+def test_varlen_balanced_workspace_contents_do_not_matter(gpu_lib):
+    """A workspace full of 0xFF, and one reused after a different batch, give
+    the same bits as a fresh one; a workspace one byte short is rejected."""
+    lay = small_varlen(77, dtype="bf16", num_heads=16, num_kv_heads=4,
+                       prefill=((50, 20), (3, 40)), decode_lens=(1, 64, 700, 33, 129))
+    st = materialize(lay, "cuda")
+    gpu_write(st)
+    need = pa.pa_varlen_workspace_bytes(st.k_cache, st.v_cache, lay.num_seqs, lay.num_heads)
+    assert need > 0
+    args = (st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens, st.block_table,
+            lay.max_query_len, lay.max_seq_len, lay.scale)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    a = pa.pa_varlen(*args, workspace=ws)
+    ws.fill_(0xFF)
+    b = pa.pa_varlen(*args, workspace=ws)
+    other = small_varlen(78, dtype="bf16", num_heads=16, num_kv_heads=4,
+                         prefill=((20, 0),), decode_lens=(300, 5, 1000))
+    st2 = materialize(other, "cuda")
+    pa.pa_varlen(st2.k_cache, st2.v_cache, st2.q, st2.cu_seqlens_q, st2.seq_lens,
+                 st2.block_table, other.max_query_len, other.max_seq_len, other.scale,
+                 workspace=ws)
+    c = pa.pa_varlen(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    with pytest.raises(pa.PaError):
+        pa.pa_varlen(*args, workspace=ws[:need - 1])
 
 
 def test_varlen_all_decode_matches_decode_oracle(gpu_lib):

@@ -80,9 +80,12 @@ def test_validation_codes(lib):
     assert lib.pa_write_kv(byref(_cache()), one, one, one, -1, None) == -2
     # varlen: max_query_len above max_seq_len, bad causal flag
     assert lib.pa_varlen(byref(_cache()), one, one, one, one, one, 1, 4, 8, 4, 70, 64, 0.1, 1,
-                         None) == -2
+                         None, 0, None) == -2
     assert lib.pa_varlen(byref(_cache()), one, one, one, one, one, 1, 4, 8, 4, 4, 64, 0.1, 2,
-                         None) == -2
+                         None, 0, None) == -2
+    # varlen workspace size query: invalid cache or heads give 0
+    assert lib.pa_varlen_workspace_bytes(None, 4, 8) == 0
+    assert lib.pa_varlen_workspace_bytes(byref(_cache()), 4, 7) == 0
 
 
 def test_balanced_validation_codes(lib):
