@@ -36,7 +36,7 @@ namespace {
 #define PA_BAL_OCC 2
 #endif
 #ifndef PA_BAL_DEPTH
-#define PA_BAL_DEPTH 4
+#define PA_BAL_DEPTH 2
 #endif
 // Whether the head waves of a workgroup meet at a barrier every DEPTH blocks.
 #ifndef PA_BAL_SYNC
