@@ -233,7 +233,8 @@ def secondary(args):
         else:
             out = torch.empty_like(st.q)
             ws = torch.empty(pa.pa_varlen_workspace_bytes(st.k_cache, st.v_cache, lay.num_seqs,
-                                                          lay.num_heads),
+                                                          st.q.shape[0], lay.num_heads,
+                                                          st.block_table.shape[1]),
                              dtype=torch.uint8, device="cuda")
 
             def step(ev=None, st=st, lay=lay, out=out, ws=ws):

@@ -169,17 +169,22 @@ pa_status pa_decode_balanced(const pa_kv_cache *cache, void *out, const void *q,
  * Requests with n_r * group > 16 (prefill chunks) run in a tiled kernel;
  * the others in the balanced kernel of pa_decode_balanced when a workspace is
  * given (partials merged by a further kernel), else one workgroup per
- * (request, KV head).
+ * (request, KV head). With a workspace, prefill tiles whose keys span more
+ * than 512 blocks are also cut into KV splits (at most 8, longer for wider
+ * block tables) whose partials a last kernel merges [P1 §07].
  *   out, q        : [T, Hq, D] in cache->dtype
  *   cu_seqlens_q  : int32 [B + 1], cu[0] = 0, non-decreasing, cu[B] = T
  *   seq_lens      : int32 [B]; KV length including this step's n_r tokens
  *   max_query_len, max_seq_len : host upper bounds (size the launch)
  *   workspace     : NULL, or caller-owned device memory of at least
- *                   pa_varlen_workspace_bytes(...) bytes (contents need not
+ *                   pa_varlen_workspace_bytes(cache, num_seqs, num_tokens,
+ *                   num_heads, max_blocks_per_seq) bytes (contents need not
  *                   be initialised; calls in flight at once must not share
  *                   it); with more than 4096 requests it is not used
- * Too small a non-NULL workspace returns PA_ERR_WORKSPACE. */
-size_t pa_varlen_workspace_bytes(const pa_kv_cache *cache, int num_seqs, int num_heads);
+ * Too small a non-NULL workspace returns PA_ERR_WORKSPACE. The workspace
+ * query returns 0 for invalid arguments. */
+size_t pa_varlen_workspace_bytes(const pa_kv_cache *cache, int num_seqs, int num_tokens,
+                                 int num_heads, int max_blocks_per_seq);
 pa_status pa_varlen(const pa_kv_cache *cache, void *out, const void *q,
                     const int32_t *cu_seqlens_q, const int32_t *seq_lens,
                     const int32_t *block_table, int num_seqs, int num_tokens,

@@ -41,7 +41,7 @@ SIGNATURES = {
     "pa_splitk_num_splits": (_I, [_I, _I]),
     "pa_decode_splitk": (_I, [_CACHE, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "pa_lse_merge": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
-    "pa_varlen_workspace_bytes": (ctypes.c_size_t, [_CACHE, _I, _I]),
+    "pa_varlen_workspace_bytes": (ctypes.c_size_t, [_CACHE, _I, _I, _I, _I]),
     "pa_varlen": (_I, [_CACHE, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P,
                        ctypes.c_size_t, _P]),
     "pa_status_str": (ctypes.c_char_p, [_I]),

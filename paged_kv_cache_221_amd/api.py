@@ -197,10 +197,12 @@ def pa_lse_merge(o_part, lse_part, seq_lens, max_seq_len: int, split_tokens: int
     return (out, lse_out) if lse_out is not None else out
 
 
-def pa_varlen_workspace_bytes(k_cache, v_cache, num_seqs: int, num_heads: int) -> int:
+def pa_varlen_workspace_bytes(k_cache, v_cache, num_seqs: int, num_tokens: int,
+                              num_heads: int, max_blocks_per_seq: int) -> int:
     c = kv_cache_struct(k_cache, v_cache)
-    return int(_native.load().pa_varlen_workspace_bytes(ctypes.byref(c), int(num_seqs),
-                                                        int(num_heads)))
+    return int(_native.load().pa_varlen_workspace_bytes(
+        ctypes.byref(c), int(num_seqs), int(num_tokens), int(num_heads),
+        int(max_blocks_per_seq)))
 
 
 def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_query_len: int,
@@ -226,7 +228,7 @@ def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_quer
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError('workspace must be "auto", None or a uint8 GPU tensor')
-        need = pa_varlen_workspace_bytes(k_cache, v_cache, b, hq)
+        need = pa_varlen_workspace_bytes(k_cache, v_cache, b, t, hq, max_blocks)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)

@@ -58,6 +58,8 @@ AttnArgs base_args(const pa_kv_cache* c, const void* q, const int32_t* block_tab
   a.num_tiles = 1;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.causal = 1;
+  a.pf_splits = 1;  // prefill tiles unsplit unless a workspace holds partials
+  a.pf_split_blocks = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
   return a;
 }
 
@@ -124,6 +126,26 @@ BalancedLayout balanced_layout(int tw, int slot_rows, int head_dim, int num_seqs
 // Rows per partial slot of the balanced kernel on a varlen batch: every
 // request that fits one 16-row tile, whatever max_query_len says.
 int varlen_slot_rows(int group) { return (pa::kTileRows / group) * group; }
+
+// Varlen workspace: the balanced kernel's part, then the prefill split
+// partials [T, Hq, splits, D] and LSEs [T, Hq, splits] (splits from the block
+// table's width, which bounds every request's keys).
+struct VarlenLayout {
+  BalancedLayout bal;
+  int pf_splits, pf_split_blocks;
+  size_t pf_o, pf_lse, total;
+};
+VarlenLayout varlen_layout(int tw, int group, int head_dim, int num_seqs, int num_kv_heads,
+                           int num_tokens, int num_heads, int max_blocks_per_seq) {
+  VarlenLayout l;
+  l.bal = balanced_layout(tw, varlen_slot_rows(group), head_dim, num_seqs, num_kv_heads);
+  pa::prefill_splits(max_blocks_per_seq, &l.pf_splits, &l.pf_split_blocks);
+  const size_t rows = (size_t)num_tokens * num_heads * (l.pf_splits > 1 ? l.pf_splits : 0);
+  l.pf_o = l.bal.total;
+  l.pf_lse = l.pf_o + align256(rows * head_dim * sizeof(float));
+  l.total = l.pf_lse + align256(rows * sizeof(float));
+  return l;
+}
 
 }  // namespace
 
@@ -235,17 +257,18 @@ pa_status pa_lse_merge(void* out, float* lse_out, const float* o_part, const flo
   return launched(pa::launch_lse_merge(a, out_dtype, static_cast<hipStream_t>(stream)));
 }
 
-size_t pa_varlen_workspace_bytes(const pa_kv_cache* cache, int num_seqs, int num_heads) {
-  if (check_cache(cache) != PA_OK || num_seqs < 0 || num_heads <= 0 ||
-      num_heads % cache->num_kv_heads != 0)
+size_t pa_varlen_workspace_bytes(const pa_kv_cache* cache, int num_seqs, int num_tokens,
+                                 int num_heads, int max_blocks_per_seq) {
+  if (check_cache(cache) != PA_OK || num_seqs < 0 || num_tokens < 0 || num_heads <= 0 ||
+      max_blocks_per_seq < 0 || num_heads % cache->num_kv_heads != 0)
     return 0;
   if (cache->head_dim != 64 && cache->head_dim != 128) return 0;
   const int group = num_heads / cache->num_kv_heads;
   if (group > pa::kTileRows) return 0;
   const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
   if (tw <= 0) return 0;
-  return balanced_layout(tw, varlen_slot_rows(group), cache->head_dim, num_seqs,
-                         cache->num_kv_heads)
+  return varlen_layout(tw, group, cache->head_dim, num_seqs, cache->num_kv_heads, num_tokens,
+                       num_heads, max_blocks_per_seq)
       .total;
 }
 
@@ -272,25 +295,41 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
   a.causal = causal;
   a.split_blocks = max_blocks_per_seq;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  // prefill chunks (query rows x group > 16): the LDS-staged prefill kernel
+  const bool use_ws = workspace != nullptr && num_seqs <= pa::kMaxBalancedSeqs;
+  VarlenLayout vl{};
+  int tw = 0;
+  if (use_ws) {
+    tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
+    if (tw <= 0) return PA_ERR_LAUNCH;
+    vl = varlen_layout(tw, a.group, cache->head_dim, num_seqs, cache->num_kv_heads, num_tokens,
+                       num_heads, max_blocks_per_seq);
+    if (workspace_bytes < vl.total) return PA_ERR_WORKSPACE;
+  }
+  char* ws = static_cast<char*>(workspace);
+  // prefill chunks (query rows x group > 16): the LDS-staged prefill kernel,
+  // long tiles cut into KV splits when the workspace holds their partials
   if ((int64_t)max_query_len * a.group > 16) {
     const int tt = pa::prefill_tile_tokens(cache->dtype, a.group);
     a.num_tiles = (max_query_len + tt - 1) / tt;
-    const int64_t pgrid = (int64_t)a.num_tiles * num_seqs * cache->num_kv_heads;
+    if (use_ws && vl.pf_splits > 1) {
+      a.pf_splits = vl.pf_splits;
+      a.pf_split_blocks = vl.pf_split_blocks;
+      a.pf_o = reinterpret_cast<float*>(ws + vl.pf_o);
+      a.pf_lse = reinterpret_cast<float*>(ws + vl.pf_lse);
+    }
+    const int64_t pgrid =
+        (int64_t)a.num_tiles * num_seqs * cache->num_kv_heads * a.pf_splits;
     if (pgrid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-    const pa_status ps = launched(pa::launch_prefill(a, cache->dtype, cache->head_dim, pgrid, st));
+    pa_status ps = launched(pa::launch_prefill(a, cache->dtype, cache->head_dim, pgrid, st));
+    if (ps != PA_OK) return ps;
+    ps = launched(pa::launch_prefill_merge(a, cache->dtype, cache->head_dim, st));
     if (ps != PA_OK) return ps;
   }
   // single-tile requests (decode rows and short queries)
-  if (workspace != nullptr && num_seqs <= pa::kMaxBalancedSeqs) {
+  if (use_ws) {
     // balanced over the whole batch's KV, head groups read together
-    const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
-    if (tw <= 0) return PA_ERR_LAUNCH;
     const int slot_rows = varlen_slot_rows(a.group);
-    const BalancedLayout lay =
-        balanced_layout(tw, slot_rows, cache->head_dim, num_seqs, cache->num_kv_heads);
-    if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
-    char* ws = static_cast<char*>(workspace);
+    const BalancedLayout& lay = vl.bal;
     pa::BalancedArgs b{};
     b.k_cache = cache->k_cache;
     b.v_cache = cache->v_cache;

@@ -31,6 +31,13 @@ struct AttnArgs {
   int num_tiles;             // query tiles per request (varlen)
   float scale_log2;          // scale * log2(e)
   int causal;
+  // Prefill KV splits: a prefill tile whose keys span more than
+  // pf_split_blocks blocks is processed as several splits that write
+  // partials here (else every tile writes its output directly).
+  float* pf_o;               // [T, Hq, pf_splits, D] normalised partial outputs, or nullptr
+  float* pf_lse;             // [T, Hq, pf_splits] partial LSEs (log2 domain)
+  int pf_splits;             // splits per tile (1: no splits)
+  int pf_split_blocks;       // KV blocks per split
 };
 
 struct MergeArgs {
@@ -101,6 +108,12 @@ hipError_t launch_attention(const AttnArgs& args, pa_dtype dtype, int head_dim, 
 hipError_t launch_lse_merge(const MergeArgs& args, pa_dtype out_dtype, hipStream_t stream);
 // Query tokens one prefill workgroup covers for GQA group size `group`.
 int prefill_tile_tokens(pa_dtype dtype, int group);
+// Prefill KV splits for keys up to max_blocks blocks: *splits splits of
+// *split_blocks blocks (*splits == 1: none).
+void prefill_splits(int max_blocks, int* splits, int* split_blocks);
+// Merges the split partials of prefill tiles into `a.out`.
+hipError_t launch_prefill_merge(const AttnArgs& a, pa_dtype dtype, int head_dim,
+                                hipStream_t stream);
 hipError_t launch_prefill(const AttnArgs& args, pa_dtype dtype, int head_dim, int64_t grid,
                           hipStream_t stream);
 // Resident waves of the balanced decode kernel on the current device for

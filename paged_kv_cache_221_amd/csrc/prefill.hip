@@ -22,6 +22,17 @@
 #ifndef PA_PREFILL_OCC
 #define PA_PREFILL_OCC 2
 #endif
+// KV blocks per split of a long prefill tile, and the most splits per tile
+// (longer contexts get longer splits). Splits only pay when the prefill
+// tiles cannot fill the GPU: on the mixed step (4 chunks of 512 tokens on
+// contexts up to 4k, 512 workgroups) 96-block splits made the prefill slower
+// (254 -> 280 us), because its workgroups already keep every CU busy.
+#ifndef PA_PREFILL_SPLIT_BLOCKS
+#define PA_PREFILL_SPLIT_BLOCKS 512
+#endif
+#ifndef PA_PREFILL_MAX_SPLITS
+#define PA_PREFILL_MAX_SPLITS 8
+#endif
 
 namespace pa {
 namespace {
@@ -60,6 +71,8 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
   int u = blockIdx.x;
   const int kvh = u % a.num_kv_heads;
   u /= a.num_kv_heads;
+  const int split = u % a.pf_splits;
+  u /= a.pf_splits;
   const int r = u % a.num_seqs;
   const int tile = a.num_tiles - 1 - u / a.num_seqs;
 
@@ -79,6 +92,11 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
   const int kmax = a.causal ? min(ctx + tile_end, seq_len) : seq_len;
   const int nblk = (kmax + kBlockTokens - 1) / kBlockTokens;
   if (nblk <= 0) return;
+  // this workgroup's blocks [b0, b1) of the tile's nblk
+  const int nsplit = a.pf_splits > 1 ? (nblk + a.pf_split_blocks - 1) / a.pf_split_blocks : 1;
+  if (split >= nsplit) return;
+  const int b0 = nsplit > 1 ? split * a.pf_split_blocks : 0;
+  const int b1 = nsplit > 1 ? min(b0 + a.pf_split_blocks, nblk) : nblk;
 
   // this wave's row tiles
   const int row = lane & 15, grp = lane >> 4;
@@ -106,8 +124,8 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
   const __attribute__((address_space(4))) int32_t* tab =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)r * a.max_blocks);
   auto issue = [&](typename St::Regs& rg, int i) {
-    const int pb = tab[min(i, nblk - 1)];
-    const bool ok = i < nblk && pb >= 0 && pb < a.num_blocks;
+    const int pb = tab[min(i, b1 - 1)];
+    const bool ok = i < b1 && pb >= 0 && pb < a.num_blocks;
     const int keys = min(seq_len - i * kBlockTokens, kBlockTokens);
     const int range = ok ? keys * row_bytes_g : 0;
     const int64_t base = (int64_t)(ok ? pb : 0) * block_elems;
@@ -137,8 +155,8 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
 
   typename St::Regs ring[RING];
 #pragma unroll
-  for (int j = 0; j < RING; ++j) issue(ring[j], j);
-  for (int i0 = 0; i0 < nblk; i0 += RING) {
+  for (int j = 0; j < RING; ++j) issue(ring[j], b0 + j);
+  for (int i0 = b0; i0 < b1; i0 += RING) {
 #pragma unroll
     for (int j = 0; j < RING; ++j) {
       const int i = i0 + j;
@@ -148,16 +166,18 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
       __builtin_amdgcn_sched_barrier(0);
       issue(ring[j], i + RING);
       __builtin_amdgcn_sched_barrier(0);
-      // Unconditional, like the loads: a padding block past nblk was read as
-      // zeros and is fully masked (every key_end is at most nblk * 16), so it
-      // adds nothing, and the accumulators stay in one set of registers.
+      // Unconditional, like the loads: a padding block past b1 was read as
+      // zeros and is fully masked (b1 < nblk only before the last split,
+      // whose keys come after), so it adds nothing, and the accumulators stay
+      // in one set of registers.
       typename O::KV kv;
       O::load_lds(kv, s_k[buf], s_v[buf], St::kLdsRow, lane);
       consume_block_tiles<E, D, RT>(st, kv, q, i * kBlockTokens, key_end, a.scale_log2, lane);
     }
   }
 
-  // epilogue: normalise and store every valid row
+  // epilogue: normalise and store every valid row (a split's partial when
+  // the tile has several splits)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     st[rt].l = sum_xor16(st[rt].l);
@@ -166,16 +186,100 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
     const int tok = tok0 + row / g, hh = row - (row / g) * g;
     if (row < tpw * g && tok < n) {
       const float inv = st[rt].l > 0.f ? 1.f / st[rt].l : 0.f;
-      S* dst = static_cast<S*>(a.out) +
-               ((int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh) * D + (D / 4) * grp;
+      const int64_t orow = (int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh;
+      if (nsplit == 1) {
+        S* dst = static_cast<S*>(a.out) + orow * D + (D / 4) * grp;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v[D / 16];
+        for (int i = 0; i < 4; ++i) {
+          float v[D / 16];
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) v[c] = st[rt].o[c][i] * inv;
-        store_chunk<E, D>(dst + (D / 16) * i, v);
+          for (int c = 0; c < D / 16; ++c) v[c] = st[rt].o[c][i] * inv;
+          store_chunk<E, D>(dst + (D / 16) * i, v);
+        }
+      } else {
+        const int64_t prow = orow * a.pf_splits + split;
+        float* dst = a.pf_o + prow * D + (D / 4) * grp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < D / 16; c += 4)
+            *reinterpret_cast<f32x4*>(dst + (D / 16) * i + c) =
+                f32x4{st[rt].o[c][i] * inv, st[rt].o[c + 1][i] * inv, st[rt].o[c + 2][i] * inv,
+                      st[rt].o[c + 3][i] * inv};
+        if (grp == 0) a.pf_lse[prow] = st[rt].l > 0.f ? st[rt].m + fast_log2(st[rt].l) : neg_inf();
       }
     }
+  }
+}
+
+// Merges the splits of long prefill tiles [P1 §07 LSE merge]: one wave per
+// (query token, head). Tokens of single-tile requests and of tiles that had
+// one split were written directly and are skipped. The tile's split count is
+// recomputed exactly as prefill_kernel derives it; it never exceeds
+// pf_splits because keys are clipped to the block table's width, from which
+// pf_splits is sized.
+template <class E>
+__global__ __launch_bounds__(4 * kWave) void prefill_merge_kernel(const AttnArgs a,
+                                                                  int tile_tokens, int D) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (unit >= (int64_t)a.num_tokens * a.num_heads) return;
+  const int token = (int)(unit / a.num_heads);
+  // the request holding this token: the largest r with cu[r] <= token
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_seqlens[mid] <= token) lo = mid; else hi = mid - 1;
+  }
+  const int r = lo;
+  int q_lo = a.cu_seqlens[r], q_hi = a.cu_seqlens[r + 1];
+  q_lo = min(max(q_lo, 0), a.num_tokens);
+  q_hi = min(max(q_hi, q_lo), a.num_tokens);
+  if (token < q_lo || token >= q_hi) return;
+  const int n = q_hi - q_lo, g = a.group;
+  if (n * g <= 16) return;
+  const int seq_len = min(max(a.seq_lens[r], 0), a.max_blocks * kBlockTokens);
+  const int ctx = max(seq_len - n, 0);
+  const int tile_end = min(((token - q_lo) / tile_tokens + 1) * tile_tokens, n);
+  const int kmax = a.causal ? min(ctx + tile_end, seq_len) : seq_len;
+  const int nblk = (kmax + kBlockTokens - 1) / kBlockTokens;
+  const int nsplit = (nblk + a.pf_split_blocks - 1) / a.pf_split_blocks;
+  if (nsplit <= 1) return;
+  const int64_t prow = unit * a.pf_splits;  // unit = token * Hq + head
+  const int d0 = lane, d1 = lane + kWave;
+  // outputs of every split, loaded together with the LSEs
+  float x0[PA_PREFILL_MAX_SPLITS], x1[PA_PREFILL_MAX_SPLITS];
+#pragma unroll
+  for (int j = 0; j < PA_PREFILL_MAX_SPLITS; ++j) {
+    const bool ok = j < nsplit;
+    x0[j] = ok && d0 < D ? a.pf_o[(prow + j) * D + d0] : 0.f;
+    x1[j] = ok && d1 < D ? a.pf_o[(prow + j) * D + d1] : 0.f;
+  }
+  const float lse = lane < nsplit ? a.pf_lse[prow + lane] : neg_inf();
+  float mx = lse;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, xor_shuffle(mx, m));
+  const float mu = mx == neg_inf() ? 0.f : mx;
+  const float w = lane < nsplit ? fast_exp2(lse - mu) : 0.f;
+  float wsum = w;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) wsum += xor_shuffle(wsum, m);
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < PA_PREFILL_MAX_SPLITS; ++j) {
+    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+    acc0 += wj * x0[j];  // zero past nsplit (loaded as 0, weight 0)
+    acc1 += wj * x1[j];
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  using S = typename E::storage;
+  S* out = static_cast<S*>(a.out) + unit * D;
+  if constexpr (sizeof(S) == 2) {
+    if (d0 < D) out[d0] = E::from_float(acc0 * inv);
+    if (d1 < D) out[d1] = E::from_float(acc1 * inv);
+  } else {
+    if (d0 < D) out[d0] = acc0 * inv;
+    if (d1 < D) out[d1] = acc1 * inv;
   }
 }
 
@@ -197,6 +301,28 @@ hipError_t launch_pf(const AttnArgs& a, int64_t grid, hipStream_t stream) {
 }
 
 }  // namespace
+
+void prefill_splits(int max_blocks, int* splits, int* split_blocks) {
+  int sp = (max_blocks + PA_PREFILL_SPLIT_BLOCKS - 1) / PA_PREFILL_SPLIT_BLOCKS;
+  sp = min(max(sp, 1), PA_PREFILL_MAX_SPLITS);
+  *splits = sp;
+  *split_blocks = max((max_blocks + sp - 1) / sp, 1);
+}
+
+hipError_t launch_prefill_merge(const AttnArgs& a, pa_dtype dtype, int head_dim,
+                                hipStream_t stream) {
+  const int64_t units = (int64_t)a.num_tokens * a.num_heads;
+  if (units <= 0 || a.pf_splits <= 1) return hipSuccess;
+  const int tt = prefill_tile_tokens(dtype, a.group);
+  const dim3 grid((unsigned)((units + 3) / 4)), block(4 * kWave);
+  switch (dtype) {
+    case PA_BF16: prefill_merge_kernel<Bf16><<<grid, block, 0, stream>>>(a, tt, head_dim); break;
+    case PA_F16: prefill_merge_kernel<F16><<<grid, block, 0, stream>>>(a, tt, head_dim); break;
+    case PA_F32: prefill_merge_kernel<F32><<<grid, block, 0, stream>>>(a, tt, head_dim); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 int prefill_tile_tokens(pa_dtype dtype, int group) {
   const int rt = dtype == PA_F32 ? prefill_rt<F32>() : prefill_rt<Bf16>();

@@ -251,7 +251,8 @@ def test_varlen_balanced_workspace_contents_do_not_matter(gpu_lib):
                        prefill=((50, 20), (3, 40)), decode_lens=(1, 64, 700, 33, 129))
     st = materialize(lay, "cuda")
     gpu_write(st)
-    need = pa.pa_varlen_workspace_bytes(st.k_cache, st.v_cache, lay.num_seqs, lay.num_heads)
+    need = pa.pa_varlen_workspace_bytes(st.k_cache, st.v_cache, lay.num_seqs, st.q.shape[0],
+                                        lay.num_heads, st.block_table.shape[1])
     assert need > 0
     args = (st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens, st.block_table,
             lay.max_query_len, lay.max_seq_len, lay.scale)
@@ -324,21 +325,25 @@ def test_binding_rejects_bad_arguments(gpu_lib):
                      10 ** 6, lay.scale)
 
 
+@pytest.mark.parametrize("path", ["balanced", "direct"])
 @pytest.mark.parametrize("case", [("bf16", 128, 32, 8), ("f16", 128, 8, 8), ("bf16", 64, 16, 2),
                                   ("f32", 128, 8, 2)], ids=lambda c: "-".join(map(str, c)))
-def test_varlen_long_prefill_tiles(gpu_lib, case):
+def test_varlen_long_prefill_tiles(gpu_lib, case, path):
     """Prefill chunks spanning several workgroup tiles with ragged ends, next to
-    decode rows."""
+    decode rows; the chunk on a 9,000-token context spans ~565 KV blocks, so
+    with a workspace its tiles run as two KV splits merged afterwards."""
     dtype, d, hq, hkv = case
     lay = small_varlen(400 + hq, dtype=dtype, num_heads=hq, num_kv_heads=hkv, head_dim=d,
-                       prefill=((300, 100), (129, 0), (65, 700)), decode_lens=(5, 333))
+                       prefill=((300, 100), (129, 0), (65, 700), (40, 9000)),
+                       decode_lens=(5, 333))
     st, snap, req = prepare(lay)
     gpu_write(st)
     snap.apply_oracle_write(lay)
     out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
-                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale)
+                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
+                       workspace="auto" if path == "balanced" else None)
     torch.cuda.synchronize()
     want, _ = varlen_oracle(st, snap, req)
     err = max_err(gpu_rows(out, dtype), want)
-    print(f"{lay.name}: long prefill max|err| = {err:.3e}", flush=True)
+    print(f"{lay.name} {path}: long prefill max|err| = {err:.3e}", flush=True)
     assert err <= TOL[dtype]

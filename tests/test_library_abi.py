@@ -84,8 +84,9 @@ def test_validation_codes(lib):
     assert lib.pa_varlen(byref(_cache()), one, one, one, one, one, 1, 4, 8, 4, 4, 64, 0.1, 2,
                          None, 0, None) == -2
     # varlen workspace size query: invalid cache or heads give 0
-    assert lib.pa_varlen_workspace_bytes(None, 4, 8) == 0
-    assert lib.pa_varlen_workspace_bytes(byref(_cache()), 4, 7) == 0
+    assert lib.pa_varlen_workspace_bytes(None, 4, 16, 8, 4) == 0
+    assert lib.pa_varlen_workspace_bytes(byref(_cache()), 4, 16, 7, 4) == 0
+    assert lib.pa_varlen_workspace_bytes(byref(_cache()), 4, -1, 8, 4) == 0
 
 
 def test_balanced_validation_codes(lib):
