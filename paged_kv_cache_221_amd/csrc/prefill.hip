@@ -37,7 +37,11 @@
 namespace pa {
 namespace {
 
-constexpr int kPrefillWaves = 4;
+// Waves per workgroup; each stages KV blocks for all of them.
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+constexpr int kPrefillWaves = PA_PREFILL_WAVES;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 static_assert(PA_PREFILL_RING % 4 == 0, "the ring (halved for fp32) alternates two LDS buffers");
 
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(4 * kWave) void prefill_merge_kernel(const AttnArgs
 // fp32 operands are twice the size: half the row tiles and half the ring.
 template <class E>
 constexpr int prefill_rt() {
-  return sizeof(typename E::storage) == 4 ? PA_PREFILL_RT / 2 : PA_PREFILL_RT;
+  return sizeof(typename E::storage) == 4 ? (PA_PREFILL_RT + 1) / 2 : PA_PREFILL_RT;
 }
 template <class E>
 constexpr int prefill_ring() {
