@@ -255,7 +255,80 @@ def secondary(args):
         print(f"[bench] {name}: attention {kern:.4f} ms", file=sys.stderr, flush=True)
         del st, step
         torch.cuda.empty_cache()
+    res["copy-on-write-blocks-bf16"] = bench_copy_blocks(k)
+    res["block-manager-host"] = bench_block_manager()
     return res
+
+
+def bench_copy_blocks(k: int, pairs: int = 4096):
+    """pa_copy_blocks on Llama-3-8B-shaped blocks (16 tokens x 8 KV heads x 128,
+    bf16: 32 KB per block per cache): `pairs` disjoint (source, destination)
+    pairs, as a batch of copy-on-write forks would queue. Algorithmic bytes:
+    every pair reads and writes one K and one V block."""
+    import torch
+    import paged_kv_cache_221_amd as pa
+    nb = 2 * pairs
+    kc = torch.zeros((nb, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    perm = torch.randperm(nb, generator=gen, device="cuda").to(torch.int32)
+    src_dst = torch.stack([perm[:pairs], perm[pairs:]], dim=1).contiguous()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pa.pa_copy_blocks(kc, vc, src_dst)
+        if ev is not None:
+            ev[1].record()
+    _, kern = time_steps([step], max(k, 10), 3, True)
+    nbytes = pairs * 2 * kc[0].numel() * 2 * 2
+    print(f"[bench] copy-on-write blocks: {kern:.4f} ms", file=sys.stderr, flush=True)
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"pairs": pairs, "kernel_ms": round(kern, 4),
+            "GBps": round(nbytes / (kern * 1e-3) / 1e9, 1),
+            "frac_of_8TBps": round(nbytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes}
+
+
+def bench_block_manager(steps: int = 2000):
+    """Host block-manager cost of one decode step of the Llama-3-8B batch (64
+    sequences of the bench lengths, pool of its size): every sequence appends
+    one token in one batched call, every 16th sequence also forks and frees a
+    candidate (copy-on-write), the queued copies are taken and the step's
+    block table is filled. Called through the Python binding, so ctypes
+    overhead is included."""
+    import paged_kv_cache_221_amd as pa
+    from workloads import llama3_8b_decode
+    lay = llama3_8b_decode()
+    bm = pa.BlockManager(lay.num_blocks, lay.block_size)
+    for r in range(lay.num_seqs):
+        bm.append(r, int(lay.seq_lens[r]) - 1)
+    import numpy as np
+    seqs = np.arange(lay.num_seqs, dtype=np.int64)
+    ones = np.ones(lay.num_seqs, dtype=np.int64)
+    width = int(lay.block_table.shape[1]) + 64
+    total = 0.0
+    for it in range(steps):
+        t0 = time.perf_counter()
+        bm.append_batch(seqs, ones)
+        for r in range(it % 16, lay.num_seqs, 16):   # 4 candidates fork, write, end
+            bm.fork(r, 1000 + r)
+            bm.append(1000 + r, 1)
+            bm.free(1000 + r)
+        bm.take_copies()
+        bm.block_tables(seqs, width)
+        total += time.perf_counter() - t0
+        if it % 64 == 63:   # untimed: bring the batch back to its lengths
+            for r in range(lay.num_seqs):
+                bm.free(r)
+                bm.append(r, int(lay.seq_lens[r]) - 1)
+    dt = total / steps
+    bm.close()
+    return {"sequences": lay.num_seqs, "us_per_step": round(dt * 1e6, 2),
+            "note": "one batched append of 64 sequences, 4 fork/append/free, the copy "
+                    "queue and the [64, width] block table per step, via ctypes"}
 
 
 def main():

@@ -59,7 +59,10 @@ typedef enum {
   PA_ERR_DTYPE = -3,       /* unknown dtype */
   PA_ERR_UNSUPPORTED = -4, /* valid but not implemented (see above) */
   PA_ERR_WORKSPACE = -5,   /* split-K workspace arguments inconsistent */
-  PA_ERR_LAUNCH = -6       /* the HIP runtime rejected a kernel launch */
+  PA_ERR_LAUNCH = -6,      /* the HIP runtime rejected a kernel launch */
+  PA_ERR_NO_BLOCKS = -7,   /* block manager: the pool has too few free blocks */
+  PA_ERR_SEQUENCE = -8,    /* block manager: unknown (or, for a fork, existing) id */
+  PA_ERR_HOST = -9         /* host memory allocation failed */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -191,6 +194,79 @@ pa_status pa_varlen(const pa_kv_cache *cache, void *out, const void *q,
                     int num_heads, int max_blocks_per_seq, int max_query_len,
                     int max_seq_len, float scale, int causal, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ blocks
+ * Host block manager [P2 "PagedAttention 机制深度解析": 块表, 工作流程, 写时复制;
+ * P1 §01 continuous batching]: the pool of physical KV blocks and one block
+ * table per sequence. Host memory only; no call touches the GPU. Thread-safe
+ * (one lock per manager). Sequence ids are the caller's int64 values.
+ *
+ * - An append of n tokens to a sequence (created on first use) takes a free
+ *   block only when the sequence's last block is full, appends it to the
+ *   table, and returns each token's slot = block * block_size + row, in
+ *   order: the slot_mapping of pa_write_kv.
+ * - A fork copies the parent's table for the child; every physical block
+ *   counts the tables holding it, and returns to the pool at zero.
+ * - Copy-on-write: appending to a sequence whose last block is partly filled
+ *   and shared first gives it a fresh block, queues (old, new) for
+ *   pa_copy_blocks and drops one reference from the old block. The queued
+ *   copies must run on the device before the new tokens' pa_write_kv.
+ * - Allocation order (deterministic): on a fresh pool blocks come out as
+ *   0, 1, 2, ...; freed blocks go on top of the pool and come out first; a
+ *   freed sequence releases its blocks from last to first.
+ * - An append that needs more free blocks than the pool holds returns
+ *   PA_ERR_NO_BLOCKS and changes nothing (pa_bm_blocks_needed tells the
+ *   scheduler beforehand, P1 §01). */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A pool of num_blocks blocks of block_size slots (block_size > 0); NULL on
+ * invalid arguments or allocation failure. Destroy with pa_bm_destroy. */
+pa_block_manager *pa_bm_create(int num_blocks, int block_size);
+void pa_bm_destroy(pa_block_manager *bm);
+/* Free blocks in the pool (-1 for NULL). */
+int pa_bm_num_free(const pa_block_manager *bm);
+/* Free blocks an append of num_tokens to seq would take, copy-on-write
+ * included; an unknown seq counts as empty. -1 for NULL or num_tokens < 0. */
+int64_t pa_bm_blocks_needed(const pa_block_manager *bm, int64_t seq, int64_t num_tokens);
+/* Room for num_tokens new tokens of seq; their slots go to slots[0..n). */
+pa_status pa_bm_append(pa_block_manager *bm, int64_t seq, int64_t num_tokens, int64_t *slots);
+/* pa_bm_append for seqs[i], num_tokens[i], i = 0, 1, ... in order, the
+ * slots packed one sequence after another into slots (sum of num_tokens
+ * entries). Stops at the first failure and returns its status; *num_done
+ * gets the number of sequences appended (those stay appended). */
+pa_status pa_bm_append_batch(pa_block_manager *bm, const int64_t *seqs,
+                             const int64_t *num_tokens, int num_seqs, int64_t *slots,
+                             int *num_done);
+/* The attention inputs for a batch: row i of tables[num_seqs][width] gets
+ * seqs[i]'s block table padded with 0, seq_lens[i] its length. Host arrays.
+ * PA_ERR_SEQUENCE for an unknown id, PA_ERR_SHAPE if a table is wider than
+ * width (nothing is written past row i then). */
+pa_status pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seqs, int num_seqs,
+                             int32_t *tables, int width, int32_t *seq_lens);
+/* child shares every block of parent (PA_ERR_SEQUENCE if parent is unknown
+ * or child exists). */
+pa_status pa_bm_fork(pa_block_manager *bm, int64_t parent, int64_t child);
+/* Drops seq and one reference from each of its blocks. */
+pa_status pa_bm_free(pa_block_manager *bm, int64_t seq);
+/* Tokens held by seq (-1 if unknown). */
+int64_t pa_bm_seq_len(const pa_block_manager *bm, int64_t seq);
+/* Writes up to max_blocks entries of seq's block table to out; returns the
+ * table's full length (-1 if unknown). */
+int pa_bm_block_table(const pa_block_manager *bm, int64_t seq, int32_t *out, int max_blocks);
+/* Tables holding block (-1 if out of range). */
+int pa_bm_ref_count(const pa_block_manager *bm, int block);
+/* Moves up to max_pairs queued copy-on-write pairs, oldest first, to
+ * src_dst[2k] = source, src_dst[2k + 1] = destination; returns how many. */
+int pa_bm_take_copies(pa_block_manager *bm, int32_t *src_dst, int max_pairs);
+
+/* Device block copy for copy-on-write [P2 写时复制]: for each pair k,
+ * K[dst] = K[src] and V[dst] = V[src] (whole blocks, all heads, raw bits).
+ *   src_dst   : device int32 [num_pairs][2]; pairs naming a block outside the
+ *               pool are skipped
+ * Destinations must be distinct and none may be a source in the same call
+ * (true of the pairs pa_bm_take_copies returns). One kernel on `stream`. */
+pa_status pa_copy_blocks(const pa_kv_cache *cache, const int32_t *src_dst, int num_pairs,
+                         void *stream);
 
 /* Static English text for a status code. */
 const char *pa_status_str(pa_status status);

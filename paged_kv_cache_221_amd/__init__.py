@@ -7,8 +7,10 @@ package only marshals torch tensors into those calls.
 
 from ._native import load  # noqa: F401
 from .api import (  # noqa: F401
+    BlockManager,
     PaError,
     kv_cache_struct,
+    pa_copy_blocks,
     pa_decode,
     pa_decode_balanced,
     pa_decode_balanced_workspace_bytes,

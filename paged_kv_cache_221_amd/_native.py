@@ -15,6 +15,8 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
                       "include", "pa.h")
 
 PA_OK = 0
+PA_ERR_NO_BLOCKS = -7
+PA_ERR_SEQUENCE = -8
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 
 
@@ -33,6 +35,7 @@ class PaKvCache(ctypes.Structure):
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
+_L = ctypes.c_int64
 _CACHE = ctypes.POINTER(PaKvCache)
 
 SIGNATURES = {
@@ -48,6 +51,20 @@ SIGNATURES = {
     "pa_decode_balanced_workspace_bytes": (ctypes.c_size_t, [_CACHE, _I, _I]),
     "pa_decode_balanced": (_I, [_CACHE, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, ctypes.c_size_t,
                                 _P]),
+    "pa_copy_blocks": (_I, [_CACHE, _P, _I, _P]),
+    "pa_bm_create": (_P, [_I, _I]),
+    "pa_bm_destroy": (None, [_P]),
+    "pa_bm_num_free": (_I, [_P]),
+    "pa_bm_blocks_needed": (_L, [_P, _L, _L]),
+    "pa_bm_append": (_I, [_P, _L, _L, _P]),
+    "pa_bm_append_batch": (_I, [_P, _P, _P, _I, _P, _P]),
+    "pa_bm_block_tables": (_I, [_P, _P, _I, _P, _I, _P]),
+    "pa_bm_fork": (_I, [_P, _L, _L]),
+    "pa_bm_free": (_I, [_P, _L]),
+    "pa_bm_seq_len": (_L, [_P, _L]),
+    "pa_bm_block_table": (_I, [_P, _L, _P, _I]),
+    "pa_bm_ref_count": (_I, [_P, _I]),
+    "pa_bm_take_copies": (_I, [_P, _P, _I]),
 }
 
 _lib = None

@@ -238,3 +238,124 @@ def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_quer
         float(scale), 1 if causal else 0, _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _stream(q)))
     return out
+
+
+def pa_copy_blocks(k_cache, v_cache, src_dst) -> None:
+    """Copy-on-write block copies: ``src_dst`` is an int32 GPU tensor
+    [num_pairs, 2] of (source, destination) blocks."""
+    lib = _native.load()
+    c = kv_cache_struct(k_cache, v_cache)
+    _dev(src_dst, "src_dst", torch.int32)
+    if src_dst.dim() != 2 or src_dst.shape[1] != 2:
+        raise ValueError("src_dst must be [num_pairs, 2]")
+    _check("pa_copy_blocks", lib.pa_copy_blocks(ctypes.byref(c), _ptr(src_dst),
+                                                int(src_dst.shape[0]), _stream(k_cache)))
+
+
+class BlockManager:
+    """The host block manager of libpa.so (``pa_bm_*``): a pool of
+    ``num_blocks`` KV blocks and one block table per sequence id, with
+    reference-counted sharing and copy-on-write. Host memory only."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._lib = _native.load()
+        self._h = self._lib.pa_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise ValueError("pa_bm_create failed (num_blocks >= 0, block_size > 0)")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free(self._h))
+
+    def blocks_needed(self, seq: int, num_tokens: int) -> int:
+        n = int(self._lib.pa_bm_blocks_needed(self._h, int(seq), int(num_tokens)))
+        if n < 0:
+            raise ValueError("num_tokens must be >= 0")
+        return n
+
+    def append(self, seq: int, num_tokens: int) -> list[int]:
+        """Slots of the num_tokens new tokens of seq (its slot_mapping)."""
+        slots = (ctypes.c_int64 * max(int(num_tokens), 1))()
+        _check("pa_bm_append", self._lib.pa_bm_append(self._h, int(seq), int(num_tokens),
+                                                      slots))
+        return list(slots[:int(num_tokens)])
+
+    def append_batch(self, seqs, num_tokens):
+        """One call for a step: appends num_tokens[i] to seqs[i] in order.
+        Returns the packed slots (numpy int64); raises PaError (with
+        ``num_done`` set) at the first sequence that does not fit."""
+        import numpy as np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        counts = np.ascontiguousarray(num_tokens, dtype=np.int64)
+        if seqs.shape != counts.shape or seqs.ndim != 1:
+            raise ValueError("seqs and num_tokens must be 1-D and of one length")
+        slots = np.empty(max(int(counts.sum()), 1), dtype=np.int64)
+        done = ctypes.c_int(0)
+        st = self._lib.pa_bm_append_batch(self._h, seqs.ctypes.data, counts.ctypes.data,
+                                          len(seqs), slots.ctypes.data, ctypes.byref(done))
+        if st != _native.PA_OK:
+            err = PaError("pa_bm_append_batch", st)
+            err.num_done = done.value
+            raise err
+        return slots[:int(counts.sum())]
+
+    def block_tables(self, seqs, width: int):
+        """(tables int32 [n, width], seq_lens int32 [n]) for the batch seqs,
+        host numpy arrays ready to copy to the GPU."""
+        import numpy as np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        tables = np.empty((len(seqs), int(width)), dtype=np.int32)
+        lens = np.empty(len(seqs), dtype=np.int32)
+        _check("pa_bm_block_tables", self._lib.pa_bm_block_tables(
+            self._h, seqs.ctypes.data, len(seqs), tables.ctypes.data, int(width),
+            lens.ctypes.data))
+        return tables, lens
+
+    def fork(self, parent: int, child: int) -> None:
+        _check("pa_bm_fork", self._lib.pa_bm_fork(self._h, int(parent), int(child)))
+
+    def free(self, seq: int) -> None:
+        _check("pa_bm_free", self._lib.pa_bm_free(self._h, int(seq)))
+
+    def seq_len(self, seq: int) -> int:
+        n = int(self._lib.pa_bm_seq_len(self._h, int(seq)))
+        if n < 0:
+            raise PaError("pa_bm_seq_len", _native.PA_ERR_SEQUENCE)
+        return n
+
+    def block_table(self, seq: int) -> list[int]:
+        n = int(self._lib.pa_bm_block_table(self._h, int(seq), None, 0))
+        if n < 0:
+            raise PaError("pa_bm_block_table", _native.PA_ERR_SEQUENCE)
+        out = (ctypes.c_int32 * max(n, 1))()
+        self._lib.pa_bm_block_table(self._h, int(seq), out, n)
+        return list(out[:n])
+
+    def ref_count(self, block: int) -> int:
+        r = int(self._lib.pa_bm_ref_count(self._h, int(block)))
+        if r < 0:
+            raise ValueError("block out of range")
+        return r
+
+    def take_copies(self, max_pairs: int | None = None) -> list[tuple[int, int]]:
+        """Queued copy-on-write (source, destination) pairs, oldest first: at
+        most max_pairs of them, or all with None."""
+        out = []
+        chunk = 256
+        buf = (ctypes.c_int32 * (2 * chunk))()
+        while max_pairs is None or len(out) < max_pairs:
+            want = chunk if max_pairs is None else min(chunk, int(max_pairs) - len(out))
+            k = int(self._lib.pa_bm_take_copies(self._h, buf, want))
+            out += [(buf[2 * i], buf[2 * i + 1]) for i in range(k)]
+            if k < want:
+                break
+        return out

@@ -18,6 +18,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
 SOURCES = ["attention.hip", "balanced.hip", "prefill.hip", "write_kv.hip", "lse_merge.hip",
+           "block_manager.cpp",
            "pa_api.cpp"]
 ARCH = "gfx950"
 

@@ -160,6 +160,9 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "split-K workspace arguments are inconsistent";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_NO_BLOCKS: return "not enough free KV blocks";
+    case PA_ERR_SEQUENCE: return "unknown or duplicate sequence id";
+    case PA_ERR_HOST: return "host memory allocation failed";
   }
   return "unknown status";
 }
@@ -176,6 +179,17 @@ pa_status pa_write_kv(const pa_kv_cache* cache, const void* k_new, const void* v
     return PA_ERR_UNSUPPORTED;
   return launched(pa::launch_write_kv(cache, k_new, v_new, slot_mapping, num_tokens,
                                       static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst, int num_pairs,
+                         void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (src_dst == nullptr) return PA_ERR_NULL;
+  return launched(pa::launch_copy_blocks(cache, src_dst, num_pairs,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* q,
