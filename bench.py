@@ -255,9 +255,50 @@ def secondary(args):
         print(f"[bench] {name}: attention {kern:.4f} ms", file=sys.stderr, flush=True)
         del st, step
         torch.cuda.empty_cache()
+    res["rope-write-kv-mixed-step-bf16"] = bench_rope_write(k)
     res["copy-on-write-blocks-bf16"] = bench_copy_blocks(k)
     res["block-manager-host"] = bench_block_manager()
     return res
+
+
+def bench_rope_write(k: int):
+    """pa_rope_write_kv on the mixed step's 2,168 new tokens (32 query / 8 KV
+    heads, head_dim 128, bf16, full rotary_dim, NeoX pairs). Algorithmic
+    bytes: q read and written, new K and V read and written to the cache,
+    positions, slots and each token's cos/sin row read."""
+    import torch
+    import paged_kv_cache_221_amd as pa
+    from workloads import mixed_step
+    from workloads.tensors import materialize
+    lay = mixed_step()
+    st = materialize(lay, "cuda", poison=False)
+    t = st.q.shape[0]
+    maxpos = int(lay.max_seq_len)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    ang = torch.rand((maxpos, 64), generator=gen, device="cuda") * 100
+    cos_sin = torch.cat([ang.cos(), ang.sin()], dim=1).contiguous()
+    positions = (torch.arange(t, device="cuda", dtype=torch.int32) % maxpos).contiguous()
+    q = st.q.clone()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pa.pa_rope_write_kv(st.k_cache, st.v_cache, q, st.k_new, st.v_new, st.slot_mapping,
+                            positions, cos_sin, 128, True)
+        if ev is not None:
+            ev[1].record()
+    _, kern = time_steps([step], max(k, 10), 3, True)
+    e = 2
+    nbytes = t * (2 * lay.num_heads * lay.head_dim * e + 4 * lay.num_kv_heads * lay.head_dim * e
+                  + 4 + 8 + 128 * 4)
+    print(f"[bench] rope + write: {kern:.4f} ms", file=sys.stderr, flush=True)
+    del st, q
+    torch.cuda.empty_cache()
+    return {"tokens": t, "kernel_ms": round(kern, 4),
+            "GBps": round(nbytes / (kern * 1e-3) / 1e9, 1),
+            "frac_of_8TBps": round(nbytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes}
 
 
 def bench_copy_blocks(k: int, pairs: int = 4096):

@@ -195,6 +195,28 @@ pa_status pa_varlen(const pa_kv_cache *cache, void *out, const void *q,
                     int max_seq_len, float scale, int causal, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* Rotary position embedding fused with the KV write [P2 步骤 3: RoPE puts
+ * position into attention, keeping relative positions; P1 §02 slot_mapping].
+ * For every token t with 0 <= positions[t] < max_position: each pair (a, b)
+ * of the first rotary_dim dimensions of every query and key head becomes
+ * (a cos - b sin, b cos + a sin) with cos = cos_sin[p][i], sin =
+ * cos_sin[p][rotary_dim/2 + i] for the pair's index i (fp32 arithmetic,
+ * rounded to nearest even into the cache dtype); dimensions >= rotary_dim
+ * are unchanged. q is rotated in place; the rotated K and the unchanged V go
+ * to slot_mapping[t] as in pa_write_kv (negative slot: not written). Tokens
+ * whose position is outside [0, max_position) are left untouched.
+ *   q          : [T, num_heads, D] device, cache dtype, rotated in place
+ *   k_new, v_new : [T, Hkv, D] device, cache dtype (not modified)
+ *   positions  : device int32 [T]
+ *   cos_sin    : device fp32 [max_position][rotary_dim] (cos | sin halves)
+ *   rotary_dim : even, 2 .. head_dim
+ *   neox_style : 1 pairs dimension i with i + rotary_dim/2, 0 pairs 2i with 2i+1 */
+pa_status pa_rope_write_kv(const pa_kv_cache *cache, void *q, int num_heads,
+                           const void *k_new, const void *v_new,
+                           const int64_t *slot_mapping, const int32_t *positions,
+                           const float *cos_sin, int max_position, int rotary_dim,
+                           int neox_style, int num_tokens, void *stream);
+
 /* ------------------------------------------------------------------ blocks
  * Host block manager [P2 "PagedAttention 机制深度解析": 块表, 工作流程, 写时复制;
  * P1 §01 continuous batching]: the pool of physical KV blocks and one block

@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     pa_decode_balanced_workspace_bytes,
     pa_decode_splitk,
     pa_lse_merge,
+    pa_rope_write_kv,
     pa_splitk_num_splits,
     pa_status_str,
     pa_varlen,

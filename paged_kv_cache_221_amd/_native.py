@@ -52,6 +52,7 @@ SIGNATURES = {
     "pa_decode_balanced": (_I, [_CACHE, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, ctypes.c_size_t,
                                 _P]),
     "pa_copy_blocks": (_I, [_CACHE, _P, _I, _P]),
+    "pa_rope_write_kv": (_I, [_CACHE, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "pa_bm_create": (_P, [_I, _I]),
     "pa_bm_destroy": (None, [_P]),
     "pa_bm_num_free": (_I, [_P]),

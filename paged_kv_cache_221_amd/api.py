@@ -240,6 +240,32 @@ def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_quer
     return out
 
 
+def pa_rope_write_kv(k_cache, v_cache, q, k_new, v_new, slot_mapping, positions, cos_sin,
+                     rotary_dim: int, neox_style: bool = True) -> None:
+    """Rotary embedding fused with the KV write: q [T, Hq, D] is rotated in
+    place, the rotated k_new and v_new [T, Hkv, D] go to slot_mapping.
+    ``positions`` int32 [T], ``cos_sin`` fp32 [max_position, rotary_dim]."""
+    lib = _native.load()
+    c = kv_cache_struct(k_cache, v_cache)
+    _dev(q, "q", k_cache.dtype)
+    t = slot_mapping.shape[0]
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(positions, "positions", torch.int32)
+    _dev(cos_sin, "cos_sin", torch.float32)
+    if q.dim() != 3 or q.shape[0] != t or q.shape[2] != c.head_dim:
+        raise ValueError("q must be [num_tokens, Hq, D]")
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        _dev(x, name, k_cache.dtype)
+        if tuple(x.shape) != (t, c.num_kv_heads, c.head_dim):
+            raise ValueError(f"{name} must be [num_tokens, Hkv, D]")
+    if tuple(positions.shape) != (t,) or cos_sin.dim() != 2 or cos_sin.shape[1] != rotary_dim:
+        raise ValueError("positions must be [T] and cos_sin [max_position, rotary_dim]")
+    _check("pa_rope_write_kv", lib.pa_rope_write_kv(
+        ctypes.byref(c), _ptr(q), int(q.shape[1]), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+        _ptr(positions), _ptr(cos_sin), int(cos_sin.shape[0]), int(rotary_dim),
+        1 if neox_style else 0, t, _stream(q)))
+
+
 def pa_copy_blocks(k_cache, v_cache, src_dst) -> None:
     """Copy-on-write block copies: ``src_dst`` is an int32 GPU tensor
     [num_pairs, 2] of (source, destination) blocks."""

@@ -181,6 +181,26 @@ pa_status pa_write_kv(const pa_kv_cache* cache, const void* k_new, const void* v
                                       static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_rope_write_kv(const pa_kv_cache* cache, void* q, int num_heads, const void* k_new,
+                           const void* v_new, const int64_t* slot_mapping,
+                           const int32_t* positions, const float* cos_sin, int max_position,
+                           int rotary_dim, int neox_style, int num_tokens, void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  if (num_tokens < 0 || num_heads <= 0 || max_position <= 0) return PA_ERR_SHAPE;
+  if (rotary_dim < 2 || rotary_dim % 2 != 0 || rotary_dim > cache->head_dim) return PA_ERR_SHAPE;
+  if (neox_style != 0 && neox_style != 1) return PA_ERR_SHAPE;
+  if (num_heads % cache->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || slot_mapping == nullptr ||
+      positions == nullptr || cos_sin == nullptr)
+    return PA_ERR_NULL;
+  return launched(pa::launch_rope_write_kv(cache, q, num_heads, k_new, v_new, slot_mapping,
+                                           positions, cos_sin, max_position, rotary_dim,
+                                           neox_style, num_tokens,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst, int num_pairs,
                          void* stream) {
   pa_status s = check_cache(cache);

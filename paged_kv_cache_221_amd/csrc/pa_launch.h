@@ -101,6 +101,10 @@ struct BalancedArgs {
 // Waves per workgroup the attention kernel is built for.
 constexpr int kAttnWaves[] = {1, 2, 4};
 
+hipError_t launch_rope_write_kv(const pa_kv_cache* c, void* q, int num_heads, const void* k_new,
+                                const void* v_new, const int64_t* slot_mapping,
+                                const int32_t* positions, const float* cos_sin, int max_position,
+                                int rotary_dim, int neox, int num_tokens, hipStream_t stream);
 hipError_t launch_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst, int num_pairs,
                               hipStream_t stream);
 hipError_t launch_write_kv(const pa_kv_cache* cache, const void* k_new, const void* v_new,

@@ -6,7 +6,8 @@
 // raw 16-byte vectors: the write is a bit-exact copy whatever the dtype.
 // One workgroup per token; its threads stride over the K then the V vectors.
 // The block copy moves whole blocks (block_size token rows) the same way,
-// one workgroup per (source, destination) pair.
+// one workgroup per (source, destination) pair. The rotary-embedding variant
+// of the write rotates q and K first [P2 步骤 3: RoPE].
 #include "attn_tile.h"
 #include "pa_launch.h"
 
@@ -68,7 +69,111 @@ __global__ __launch_bounds__(kWriteThreads) void copy_blocks_kernel(
   }
 }
 
+// Storage <-> fp32 for the rotary embedding (round to nearest even back).
+template <class E>
+__device__ inline float to_f32(typename E::storage v);
+template <>
+__device__ inline float to_f32<Bf16>(uint16_t v) {
+  return __uint_as_float((unsigned)v << 16);
+}
+template <>
+__device__ inline float to_f32<F16>(uint16_t v) {
+  return (float)__builtin_bit_cast(_Float16, v);
+}
+template <>
+__device__ inline float to_f32<F32>(float v) {
+  return v;
+}
+template <class E>
+__device__ inline typename E::storage from_f32(float f) {
+  if constexpr (sizeof(typename E::storage) == 4) {
+    return f;
+  } else {
+    return E::from_float(f);
+  }
+}
+
+// Rotary position embedding fused with the KV write: one workgroup per token.
+// Each rotated pair (a, b) of a query or key head becomes
+// (a cos - b sin, b cos + a sin) in fp32 with the angle of its position;
+// q is rotated in place, the rotated K and the raw V go to the token's slot.
+template <class E>
+__global__ __launch_bounds__(kWriteThreads) void rope_write_kv_kernel(
+    typename E::storage* __restrict__ q, const typename E::storage* __restrict__ k_new,
+    const typename E::storage* __restrict__ v_new, typename E::storage* __restrict__ k_cache,
+    typename E::storage* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping,
+    const int32_t* __restrict__ positions, const float* __restrict__ cos_sin, int max_position,
+    int rotary_dim, int neox, int num_heads, int num_kv_heads, int head_dim, int64_t num_slots) {
+  using S = typename E::storage;
+  const int64_t t = blockIdx.x;
+  const int pos = positions[t];
+  if (pos < 0 || pos >= max_position) return;  // outside the table: token left alone
+  const int half = rotary_dim / 2;
+  const float* cs = cos_sin + (int64_t)pos * rotary_dim;
+  auto pair = [&](int j, int* ia, int* ib) {
+    *ia = neox ? j : 2 * j;
+    *ib = neox ? j + half : 2 * j + 1;
+  };
+  // queries, in place
+  for (int i = threadIdx.x; i < num_heads * half; i += kWriteThreads) {
+    const int h = i / half, j = i - h * half;
+    int ia, ib;
+    pair(j, &ia, &ib);
+    S* row = q + (t * num_heads + h) * head_dim;
+    const float a = to_f32<E>(row[ia]), b = to_f32<E>(row[ib]);
+    const float c = cs[j], sn = cs[half + j];
+    row[ia] = from_f32<E>(a * c - b * sn);
+    row[ib] = from_f32<E>(b * c + a * sn);
+  }
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;  // padding token, or outside the pool
+  const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+  const S* ks = k_new + t * row_elems;
+  const S* vs = v_new + t * row_elems;
+  S* kd = k_cache + slot * row_elems;
+  S* vd = v_cache + slot * row_elems;
+  for (int i = threadIdx.x; i < num_kv_heads * half; i += kWriteThreads) {
+    const int h = i / half, j = i - h * half;
+    int ia, ib;
+    pair(j, &ia, &ib);
+    const float a = to_f32<E>(ks[h * head_dim + ia]), b = to_f32<E>(ks[h * head_dim + ib]);
+    const float c = cs[j], sn = cs[half + j];
+    kd[h * head_dim + ia] = from_f32<E>(a * c - b * sn);
+    kd[h * head_dim + ib] = from_f32<E>(b * c + a * sn);
+  }
+  const int rest = head_dim - rotary_dim;  // dimensions past rotary_dim pass through
+  for (int i = threadIdx.x; i < num_kv_heads * rest; i += kWriteThreads) {
+    const int h = i / rest, d = rotary_dim + (i - h * rest);
+    kd[h * head_dim + d] = ks[h * head_dim + d];
+  }
+  for (int64_t i = threadIdx.x; i < row_elems; i += kWriteThreads) vd[i] = vs[i];
+}
+
 }  // namespace
+
+hipError_t launch_rope_write_kv(const pa_kv_cache* c, void* q, int num_heads, const void* k_new,
+                                const void* v_new, const int64_t* slot_mapping,
+                                const int32_t* positions, const float* cos_sin, int max_position,
+                                int rotary_dim, int neox, int num_tokens, hipStream_t stream) {
+  if (num_tokens <= 0) return hipSuccess;
+  const int64_t num_slots = (int64_t)c->num_blocks * c->block_size;
+  const dim3 grid((unsigned)num_tokens), block(kWriteThreads);
+  switch (c->dtype) {
+#define PA_ROPE_LAUNCH(E)                                                                        \
+  rope_write_kv_kernel<E><<<grid, block, 0, stream>>>(                                          \
+      static_cast<E::storage*>(q), static_cast<const E::storage*>(k_new),                        \
+      static_cast<const E::storage*>(v_new), static_cast<E::storage*>(c->k_cache),              \
+      static_cast<E::storage*>(c->v_cache), slot_mapping, positions, cos_sin, max_position,      \
+      rotary_dim, neox, num_heads, c->num_kv_heads, c->head_dim, num_slots);                     \
+  break;
+    case PA_BF16: PA_ROPE_LAUNCH(Bf16)
+    case PA_F16: PA_ROPE_LAUNCH(F16)
+    case PA_F32: PA_ROPE_LAUNCH(F32)
+#undef PA_ROPE_LAUNCH
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_copy_blocks(const pa_kv_cache* c, const int32_t* src_dst, int num_pairs,
                               hipStream_t stream) {
