@@ -96,11 +96,13 @@ def load_traffic(src_hash: str, path_name: str):
 class DecodeStep:
     """One step on one copy of the inputs: write, then attention."""
 
-    def __init__(self, st, path: str, split_tokens: int):
+    def __init__(self, st, path: str, split_tokens: int, kv_scales=None):
         import torch
         import paged_kv_cache_221_amd as pa
         self.pa, self.torch = pa, torch
         self.st, self.path, self.split = st, path, split_tokens
+        self.kw = {} if kv_scales is None else {"k_scale": kv_scales[0],
+                                                "v_scale": kv_scales[1]}
         lay = st.layout
         self.out = torch.empty_like(st.q)
         if path == "balanced":
@@ -114,24 +116,25 @@ class DecodeStep:
             self.lse_part = torch.empty((b, hq, s), dtype=torch.float32, device=st.q.device)
 
     def __call__(self, ev=None):
-        st, pa, lay = self.st, self.pa, self.st.layout
-        pa.pa_write_kv(st.k_cache, st.v_cache, st.k_new, st.v_new, st.slot_mapping)
+        st, pa, lay, kw = self.st, self.pa, self.st.layout, self.kw
+        pa.pa_write_kv(st.k_cache, st.v_cache, st.k_new, st.v_new, st.slot_mapping, **kw)
         if ev is not None:
             ev[0].record()
         if self.path == "decode":
             pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
-                         lay.max_seq_len, lay.scale, out=self.out)
+                         lay.max_seq_len, lay.scale, out=self.out, **kw)
             if ev is not None:
                 ev[1].record()
         elif self.path == "balanced":
             pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
-                                  lay.max_seq_len, lay.scale, workspace=self.ws, out=self.out)
+                                  lay.max_seq_len, lay.scale, workspace=self.ws, out=self.out,
+                                  **kw)
             if ev is not None:
                 ev[1].record()
         else:
             pa.pa_decode_splitk(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
                                 lay.max_seq_len, self.split, lay.scale, o_part=self.o_part,
-                                lse_part=self.lse_part)
+                                lse_part=self.lse_part, **kw)
             if ev is not None:
                 ev[1].record()
             pa.pa_lse_merge(self.o_part, self.lse_part, st.seq_lens, lay.max_seq_len,
@@ -255,10 +258,39 @@ def secondary(args):
         print(f"[bench] {name}: attention {kern:.4f} ms", file=sys.stderr, flush=True)
         del st, step
         torch.cuda.empty_cache()
+    res["llama3-8b-decode-e4m3-cache"] = bench_fp8_decode(k)
     res["rope-write-kv-mixed-step-bf16"] = bench_rope_write(k)
     res["copy-on-write-blocks-bf16"] = bench_copy_blocks(k)
     res["block-manager-host"] = bench_block_manager()
     return res
+
+
+def bench_fp8_decode(k: int, copies: int = 4):
+    """The Llama-3-8B decode batch with an E4M3 KV cache (bf16 q and output),
+    balanced path. Algorithmic bytes: one byte per cached K/V element, bf16 q
+    in and out, block-table entries and seq_lens."""
+    import torch
+    from workloads import llama3_8b_decode
+    from workloads.tensors import materialize_e4m3
+    lay = llama3_8b_decode()
+    scales = (0.0625, 0.0625)
+    sts = [materialize_e4m3(lay, "cuda", *scales, poison=False, seed_offset=i)
+           for i in range(copies)]
+    steps = [DecodeStep(st, "balanced", 0, kv_scales=scales) for st in sts]
+    ms, kern = time_steps(steps, max(k, 10), 3, True)
+    kvb = 2 * lay.num_kv_heads * lay.head_dim
+    lens = lay.seq_lens.astype("int64")
+    blocks = (lens + lay.block_size - 1) // lay.block_size
+    nbytes = int(lens.sum() * kvb + 2 * lay.num_seqs * lay.num_heads * lay.head_dim * 2
+                 + 4 * blocks.sum() + 4 * lay.num_seqs)
+    print(f"[bench] e4m3 decode: attention {kern:.4f} ms", file=sys.stderr, flush=True)
+    del sts, steps
+    torch.cuda.empty_cache()
+    return {"step_ms": round(ms, 4), "attention_kernel_ms": round(kern, 4),
+            "attention_GBps": round(nbytes / (kern * 1e-3) / 1e9, 1),
+            "attention_frac_of_8TBps": round(nbytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes,
+            "decode_tokens_per_s_per_layer": round(lay.num_seqs / (kern * 1e-3), 1)}
 
 
 def bench_rope_write(k: int):

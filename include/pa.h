@@ -39,7 +39,10 @@
  *   max_blocks_per_seq * bs.
  *   Results for such inputs are unspecified.
  * - Supported now: block_size 16; head_dim 64 or 128; Hq % Hkv == 0 with
- *   Hq / Hkv <= 16; fp32, fp16 and bf16 storage with fp32 accumulation.
+ *   Hq / Hkv <= 16; fp32, fp16 and bf16 storage with fp32 accumulation, and
+ *   E4M3 KV caches (bf16 arithmetic on the exactly widened codes) in
+ *   pa_write_kv, pa_copy_blocks, pa_decode, pa_decode_splitk,
+ *   pa_decode_balanced and pa_varlen batches without prefill chunks.
  *   Anything else returns PA_ERR_UNSUPPORTED.
  */
 #ifndef PA_H
@@ -65,7 +68,11 @@ typedef enum {
   PA_ERR_HOST = -9         /* host memory allocation failed */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* Storage types. PA_FP8_E4M3 is a KV cache of OCP E4M3 codes (8-bit float:
+ * sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 0x7f /
+ * 0xff NaN, largest finite 448) holding x / scale, with the per-layer scales
+ * of pa_kv_cache; queries, new K/V rows and outputs are then bf16. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* One layer's paged KV cache [P1 §02]: the pages' pool
  * [num_layers, 2, num_blocks, block_size, num_kv_heads, head_dim] seen for one
@@ -80,11 +87,16 @@ typedef struct {
   int num_kv_heads;
   int head_dim;
   pa_dtype dtype;
+  float k_scale; /* PA_FP8_E4M3 only: K = code * k_scale (finite, > 0) */
+  float v_scale; /* PA_FP8_E4M3 only: V = code * v_scale (finite, > 0) */
 } pa_kv_cache;
 
 /* KV write [P1 §02; P3 §1.4]: for each token i with s = slot_mapping[i] >= 0,
- * copy k_new[i] to K slot s and v_new[i] to V slot s, bit for bit.
- *   k_new, v_new : [T, Hkv, D] in cache->dtype
+ * copy k_new[i] to K slot s and v_new[i] to V slot s, bit for bit. For an
+ * E4M3 cache the rows are bf16 and each element x is stored as the E4M3 code
+ * nearest to the fp32 quotient x / scale (ties to the even code, magnitudes
+ * of 448 and more saturate to 448, NaN stays NaN).
+ *   k_new, v_new : [T, Hkv, D] in cache->dtype (bf16 for an E4M3 cache)
  *   slot_mapping : int64 [T]; a negative entry means "do not write"
  * T == 0 is a no-op. */
 pa_status pa_write_kv(const pa_kv_cache *cache, const void *k_new, const void *v_new,

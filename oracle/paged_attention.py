@@ -45,8 +45,10 @@ from __future__ import annotations
 
 import numpy as np
 
-# Raw-bit storage type for each stored dtype.
-STORAGE_DTYPES = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
+from . import fp8
+
+# Raw-bit storage type for each stored dtype ("e4m3": 8-bit float cache codes).
+STORAGE_DTYPES = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
 
 
 def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
@@ -63,6 +65,8 @@ def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         wide = bits.astype(np.uint32) << np.uint32(16)
         return wide.view(np.float32).astype(np.float64)
+    if dtype == "e4m3":
+        return fp8.decode(bits)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -144,22 +148,30 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     return out, lse
 
 
-def _request_kv(k_cache, v_cache, table_row, length, block_size, dtype):
-    kr = widen(gather_blocks(k_cache, table_row, length, block_size), dtype)
-    vr = widen(gather_blocks(v_cache, table_row, length, block_size), dtype)
+def _request_kv(k_cache, v_cache, table_row, length, block_size, dtype, kv_dtype=None,
+                k_scale=1.0, v_scale=1.0):
+    """A request's K and V in float64. With ``kv_dtype`` given (a quantised
+    cache, [P3 §4.1]) the cache holds codes of that type and an element is its
+    code's value times the cache's scale; ``dtype`` is then the queries'."""
+    if kv_dtype is None:
+        kr = widen(gather_blocks(k_cache, table_row, length, block_size), dtype)
+        vr = widen(gather_blocks(v_cache, table_row, length, block_size), dtype)
+        return kr, vr
+    kr = widen(gather_blocks(k_cache, table_row, length, block_size), kv_dtype) * k_scale
+    vr = widen(gather_blocks(v_cache, table_row, length, block_size), kv_dtype) * v_scale
     return kr, vr
 
 
 def paged_decode(q_bits: np.ndarray, k_cache, v_cache, block_table: np.ndarray,
                  seq_lens: np.ndarray, scale: float, block_size: int, dtype: str,
-                 requests=None):
+                 requests=None, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Decode attention: one query row per request against its whole KV.
 
     [P1 §04 table]: decode has query_len 1 and seq_len = all history tokens
     (the token being decoded included, written before it is read [P3 §1.4]).
     ``q_bits [B, Hq, D]``. Returns ``(out [B, Hq, D], lse [B, Hq])`` float64;
     with ``requests`` given, only those rows are computed (the rest stay 0 /
-    -inf).
+    -inf). ``kv_dtype`` / ``k_scale`` / ``v_scale``: a quantised cache.
     """
     bsz, hq, d = q_bits.shape
     out = np.zeros((bsz, hq, d), dtype=np.float64)
@@ -168,7 +180,8 @@ def paged_decode(q_bits: np.ndarray, k_cache, v_cache, block_table: np.ndarray,
         length = int(seq_lens[r])
         if length == 0:
             continue
-        kr, vr = _request_kv(k_cache, v_cache, block_table[r], length, block_size, dtype)
+        kr, vr = _request_kv(k_cache, v_cache, block_table[r], length, block_size, dtype,
+                             kv_dtype, k_scale, v_scale)
         o, s = attend(widen(q_bits[r:r + 1], dtype), kr, vr, scale, causal=True)
         out[r], lse[r] = o[0], s[0]
     return out, lse
@@ -176,7 +189,8 @@ def paged_decode(q_bits: np.ndarray, k_cache, v_cache, block_table: np.ndarray,
 
 def paged_varlen(q_bits: np.ndarray, k_cache, v_cache, cu_seqlens_q: np.ndarray,
                  seq_lens: np.ndarray, block_table: np.ndarray, scale: float,
-                 block_size: int, dtype: str, causal: bool = True, requests=None):
+                 block_size: int, dtype: str, causal: bool = True, requests=None,
+                 kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Flattened varlen step: request r owns rows ``cu[r]:cu[r+1]`` of ``q``.
 
     [P1 §03/§04]: no padding, requests isolated by the cumulative lengths;
@@ -195,7 +209,8 @@ def paged_varlen(q_bits: np.ndarray, k_cache, v_cache, cu_seqlens_q: np.ndarray,
             continue
         if length < hi - lo:
             raise ValueError(f"request {r}: seq_len {length} < query_len {hi - lo}")
-        kr, vr = _request_kv(k_cache, v_cache, block_table[r], length, block_size, dtype)
+        kr, vr = _request_kv(k_cache, v_cache, block_table[r], length, block_size, dtype,
+                             kv_dtype, k_scale, v_scale)
         o, s = attend(widen(q_bits[lo:hi], dtype), kr, vr, scale, causal=causal)
         out[lo:hi], lse[lo:hi] = o, s
     return out, lse
@@ -203,7 +218,8 @@ def paged_varlen(q_bits: np.ndarray, k_cache, v_cache, cu_seqlens_q: np.ndarray,
 
 def splitk_partials(q_bits: np.ndarray, k_cache, v_cache, block_table: np.ndarray,
                     seq_lens: np.ndarray, scale: float, block_size: int, dtype: str,
-                    split_tokens: int, max_splits: int, requests=None):
+                    split_tokens: int, max_splits: int, requests=None, kv_dtype=None,
+                    k_scale=1.0, v_scale=1.0):
     """Per-split normalised outputs and LSEs of decode attention [P1 §07].
 
     Split j of request r covers tokens ``[j*S, min((j+1)*S, L_r))``.
@@ -217,7 +233,8 @@ def splitk_partials(q_bits: np.ndarray, k_cache, v_cache, block_table: np.ndarra
         length = int(seq_lens[r])
         if length == 0:
             continue
-        kr, vr = _request_kv(k_cache, v_cache, block_table[r], length, block_size, dtype)
+        kr, vr = _request_kv(k_cache, v_cache, block_table[r], length, block_size, dtype,
+                             kv_dtype, k_scale, v_scale)
         qr = widen(q_bits[r:r + 1], dtype)
         for j in range(max_splits):
             lo, hi = j * split_tokens, min((j + 1) * split_tokens, length)

@@ -29,6 +29,8 @@ class PaKvCache(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int),
         ("head_dim", ctypes.c_int),
         ("dtype", ctypes.c_int),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 

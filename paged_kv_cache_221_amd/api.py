@@ -16,7 +16,13 @@ import torch
 
 from . import _native
 
-_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2,
+               torch.float8_e4m3fn: 3}
+
+
+def _act_dtype(k_cache: torch.Tensor):
+    """dtype of q, outputs and new K/V rows: the cache's, bf16 for an E4M3 cache."""
+    return torch.bfloat16 if k_cache.dtype == torch.float8_e4m3fn else k_cache.dtype
 
 
 class PaError(RuntimeError):
@@ -51,8 +57,11 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def kv_cache_struct(k_cache: torch.Tensor, v_cache: torch.Tensor) -> _native.PaKvCache:
-    """``pa_kv_cache`` for one layer's K and V pools ``[num_blocks, bs, Hkv, D]``."""
+def kv_cache_struct(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float = 1.0,
+                    v_scale: float = 1.0) -> _native.PaKvCache:
+    """``pa_kv_cache`` for one layer's K and V pools ``[num_blocks, bs, Hkv, D]``.
+    ``k_scale`` / ``v_scale`` are the dequantisation scales of an E4M3 cache
+    (stored code * scale = value); other caches ignore them."""
     _dev(k_cache, "k_cache")
     _dev(v_cache, "v_cache", k_cache.dtype)
     if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
@@ -63,20 +72,21 @@ def kv_cache_struct(k_cache: torch.Tensor, v_cache: torch.Tensor) -> _native.PaK
         raise ValueError("k_cache and v_cache must be on one device")
     nb, bs, hkv, d = k_cache.shape
     return _native.PaKvCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, d,
-                             _DTYPE_CODE[k_cache.dtype])
+                             _DTYPE_CODE[k_cache.dtype], float(k_scale), float(v_scale))
 
 
 def pa_status_str(status: int) -> str:
     return _native.load().pa_status_str(status).decode()
 
 
-def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping) -> None:
+def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, k_scale: float = 1.0,
+                v_scale: float = 1.0) -> None:
     lib = _native.load()
-    c = kv_cache_struct(k_cache, v_cache)
+    c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
     t = slot_mapping.shape[0]
     _dev(slot_mapping, "slot_mapping", torch.int64)
     for name, x in (("k_new", k_new), ("v_new", v_new)):
-        _dev(x, name, k_cache.dtype)
+        _dev(x, name, _act_dtype(k_cache))
         if tuple(x.shape) != (t, c.num_kv_heads, c.head_dim):
             raise ValueError(f"{name} must be [num_tokens, Hkv, D]")
     _check("pa_write_kv", lib.pa_write_kv(ctypes.byref(c), _ptr(k_new), _ptr(v_new),
@@ -94,10 +104,10 @@ def _attention_meta(c, block_table, seq_lens, num_seqs):
 
 
 def pa_decode(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int, scale: float,
-              out=None):
+              out=None, k_scale: float = 1.0, v_scale: float = 1.0):
     lib = _native.load()
-    c = kv_cache_struct(k_cache, v_cache)
-    _dev(q, "q", k_cache.dtype)
+    c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
+    _dev(q, "q", _act_dtype(k_cache))
     if q.dim() != 3 or q.shape[2] != c.head_dim:
         raise ValueError("q must be [num_seqs, Hq, D]")
     b, hq, _ = q.shape
@@ -118,13 +128,14 @@ def pa_decode_balanced_workspace_bytes(k_cache, v_cache, num_seqs: int, num_head
 
 
 def pa_decode_balanced(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int,
-                       scale: float, workspace=None, out=None):
+                       scale: float, workspace=None, out=None, k_scale: float = 1.0,
+                       v_scale: float = 1.0):
     """Balanced decode; ``workspace`` is a uint8 GPU tensor of at least
     ``pa_decode_balanced_workspace_bytes`` bytes (allocated here if None); its
     contents need not be initialised."""
     lib = _native.load()
-    c = kv_cache_struct(k_cache, v_cache)
-    _dev(q, "q", k_cache.dtype)
+    c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
+    _dev(q, "q", _act_dtype(k_cache))
     if q.dim() != 3 or q.shape[2] != c.head_dim:
         raise ValueError("q must be [num_seqs, Hq, D]")
     b, hq, _ = q.shape
@@ -148,10 +159,11 @@ def pa_splitk_num_splits(max_seq_len: int, split_tokens: int) -> int:
 
 
 def pa_decode_splitk(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int,
-                     split_tokens: int, scale: float, o_part=None, lse_part=None):
+                     split_tokens: int, scale: float, o_part=None, lse_part=None,
+                     k_scale: float = 1.0, v_scale: float = 1.0):
     lib = _native.load()
-    c = kv_cache_struct(k_cache, v_cache)
-    _dev(q, "q", k_cache.dtype)
+    c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
+    _dev(q, "q", _act_dtype(k_cache))
     if q.dim() != 3 or q.shape[2] != c.head_dim:
         raise ValueError("q must be [num_seqs, Hq, D]")
     b, hq, d = q.shape
@@ -206,14 +218,15 @@ def pa_varlen_workspace_bytes(k_cache, v_cache, num_seqs: int, num_tokens: int,
 
 
 def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_query_len: int,
-              max_seq_len: int, scale: float, causal: bool = True, out=None, workspace="auto"):
+              max_seq_len: int, scale: float, causal: bool = True, out=None, workspace="auto",
+              k_scale: float = 1.0, v_scale: float = 1.0):
     """Varlen step. ``workspace``: "auto" allocates one of
     ``pa_varlen_workspace_bytes`` bytes (the balanced path for single-tile
     requests), None passes NULL (one workgroup per request and KV head), or a
     uint8 GPU tensor."""
     lib = _native.load()
-    c = kv_cache_struct(k_cache, v_cache)
-    _dev(q, "q", k_cache.dtype)
+    c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
+    _dev(q, "q", _act_dtype(k_cache))
     if q.dim() != 3 or q.shape[2] != c.head_dim:
         raise ValueError("q must be [num_tokens, Hq, D]")
     t, hq, _ = q.shape
@@ -247,7 +260,7 @@ def pa_rope_write_kv(k_cache, v_cache, q, k_new, v_new, slot_mapping, positions,
     ``positions`` int32 [T], ``cos_sin`` fp32 [max_position, rotary_dim]."""
     lib = _native.load()
     c = kv_cache_struct(k_cache, v_cache)
-    _dev(q, "q", k_cache.dtype)
+    _dev(q, "q", _act_dtype(k_cache))
     t = slot_mapping.shape[0]
     _dev(slot_mapping, "slot_mapping", torch.int64)
     _dev(positions, "positions", torch.int32)
@@ -255,7 +268,7 @@ def pa_rope_write_kv(k_cache, v_cache, q, k_new, v_new, slot_mapping, positions,
     if q.dim() != 3 or q.shape[0] != t or q.shape[2] != c.head_dim:
         raise ValueError("q must be [num_tokens, Hq, D]")
     for name, x in (("k_new", k_new), ("v_new", v_new)):
-        _dev(x, name, k_cache.dtype)
+        _dev(x, name, _act_dtype(k_cache))
         if tuple(x.shape) != (t, c.num_kv_heads, c.head_dim):
             raise ValueError(f"{name} must be [num_tokens, Hkv, D]")
     if tuple(positions.shape) != (t,) or cos_sin.dim() != 2 or cos_sin.shape[1] != rotary_dim:

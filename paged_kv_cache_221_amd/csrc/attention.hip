@@ -53,9 +53,10 @@ __global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const At
   const int row = lane & 15;
   const int grp = lane >> 4;
 
-  KvView<S> view;
-  view.k = static_cast<const S*>(a.k_cache) + (int64_t)kvh * D;
-  view.v = static_cast<const S*>(a.v_cache) + (int64_t)kvh * D;
+  using KS = typename O::kv_storage;
+  KvView<KS> view;
+  view.k = static_cast<const KS*>(a.k_cache) + (int64_t)kvh * D;
+  view.v = static_cast<const KS*>(a.v_cache) + (int64_t)kvh * D;
   view.rs = (int64_t)a.num_kv_heads * D;
   view.table = a.block_table + (int64_t)r * a.max_blocks;
   view.num_blocks = a.num_blocks;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const At
     const int nrows = n * g;
     auto emit = [&](int rr, int d, float acc, float lsum, float mx) {
       const int head = kvh * g + rr % g;
-      const float val = lsum > 0.f ? acc / lsum : 0.f;
+      const float val = (lsum > 0.f ? acc / lsum : 0.f) * a.out_scale;
       if (a.o_part != nullptr) {
         const int64_t unit = (int64_t)r * a.num_heads + head;
         a.o_part[(unit * a.num_splits + split) * D + d] = val;
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const At
     } else {
       if (row < nrows) {
         if (a.o_part == nullptr) {
-          const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+          const float inv = (st.l > 0.f ? 1.f / st.l : 0.f) * a.out_scale;
           S* dst = static_cast<S*>(a.out) +
                    ((int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh) * D + (D / 4) * grp;
 #pragma unroll
@@ -190,6 +191,7 @@ hipError_t launch_attention(const AttnArgs& args, pa_dtype dtype, int head_dim, 
     case PA_BF16: return launch_d<Bf16>(args, head_dim, waves, grid, stream);
     case PA_F16: return launch_d<F16>(args, head_dim, waves, grid, stream);
     case PA_F32: return launch_d<F32>(args, head_dim, waves, grid, stream);
+    case PA_FP8_E4M3: return launch_d<Fp8>(args, head_dim, waves, grid, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -84,13 +84,17 @@ __device__ inline Rsrc make_rsrc(const void* base, int range_bytes) {
 __device__ inline u32x4 buf_load16(Rsrc r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+__device__ inline unsigned buf_load4(Rsrc r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 __device__ inline u32x2 buf_load8(Rsrc r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
 
 // ----------------------------------------------------------- element types
 struct Bf16 {
-  using storage = uint16_t;
+  using storage = uint16_t;     // q, outputs
+  using kv_storage = uint16_t;  // the KV cache
   // two floats -> packed bf16 pair (round to nearest even), lo in bits 0..15
   __device__ static unsigned pack2(float lo, float hi) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -115,6 +119,7 @@ struct Bf16 {
 
 struct F16 {
   using storage = uint16_t;
+  using kv_storage = uint16_t;
   __device__ static unsigned pack2(float lo, float hi) {
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     f16x2 h = {(_Float16)lo, (_Float16)hi};
@@ -136,7 +141,27 @@ struct F16 {
 
 struct F32 {
   using storage = float;
+  using kv_storage = float;
 };
+
+// An E4M3 KV cache (OCP 8-bit float: 4 exponent bits, bias 7, 3 mantissa
+// bits, no infinities) with bf16 queries, outputs and arithmetic. Every E4M3
+// value is a bf16 value, so blocks are widened to bf16 MFMA operands exactly
+// after loading; the cache's scales are folded into the softmax scale (K)
+// and the output normalisation (V) by the caller of the kernels.
+struct Fp8 : Bf16 {
+  using kv_storage = uint8_t;
+};
+
+// Four E4M3 codes (byte k of w is element k) -> four bf16, as two packed
+// words in the same order.
+__device__ inline void fp8x4_to_bf16(unsigned w, unsigned* lo, unsigned* hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  *lo = Bf16::pack2(a.x, a.y);
+  *hi = Bf16::pack2(b.x, b.y);
+}
 
 // --------------------------------------------------- operand load / compute
 // Ops<E, D> knows how one wave loads a 16-token KV block in MFMA operand
@@ -261,15 +286,88 @@ struct Ops16 {
 };
 
 template <int D>
-struct Ops<Bf16, D> : Ops16<Bf16, D> {};
+struct Ops<Bf16, D> : Ops16<Bf16, D> {
+  using kv_storage = uint16_t;
+};
 template <int D>
-struct Ops<F16, D> : Ops16<F16, D> {};
+struct Ops<F16, D> : Ops16<F16, D> {
+  using kv_storage = uint16_t;
+};
+
+// E4M3 cache: the bf16 tile with half-size loads. The registers keep the raw
+// codes until the block is consumed (so loads stay in flight); scores() and
+// build_v() widen them to the bf16 operands of Ops16<Bf16, D>.
+template <int D>
+struct Ops<Fp8, D> : Ops16<Bf16, D> {
+  using Base = Ops16<Bf16, D>;
+  using kv_storage = uint8_t;
+  using typename Base::Q;
+  using typename Base::P;
+  using typename Base::VA;
+  static constexpr int kQk = D / 32;
+  static constexpr int kVe = D / 16;
+  struct KV {
+    u32x2 k[kQk];            // 8 codes per 32-dim chunk
+    unsigned v[4][kVe / 4];  // kVe codes of each of the lane's four key rows
+  };
+  struct Off {
+    int k[kQk];
+    int v[4];
+  };
+  __device__ static Off offsets(int64_t rs, int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+    Off o;
+#pragma unroll
+    for (int c = 0; c < kQk; ++c) o.k[c] = (int)(m * rs + 32 * c + 8 * grp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.v[i] = (int)((4 * grp + i) * rs + kVe * m);
+    return o;
+  }
+  __device__ static void load(KV& kv, Rsrc kr, Rsrc vr, const Off& o) {
+#pragma unroll
+    for (int c = 0; c < kQk; ++c) kv.k[c] = buf_load8(kr, o.k[c]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kVe == 8) {
+        const u32x2 t = buf_load8(vr, o.v[i]);
+        kv.v[i][0] = t.x;
+        kv.v[i][1] = t.y;
+      } else {
+        kv.v[i][0] = buf_load4(vr, o.v[i]);
+      }
+    }
+  }
+  __device__ static f32x4 scores(const KV& kv, const Q& q) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kQk; ++c) {
+      unsigned w0, w1, w2, w3;
+      fp8x4_to_bf16(kv.k[c].x, &w0, &w1);
+      fp8x4_to_bf16(kv.k[c].y, &w2, &w3);
+      acc = Bf16::mma_qk(u32x4{w0, w1, w2, w3}, q.q[c], acc);
+    }
+    return acc;
+  }
+  __device__ static VA build_v(const KV& kv) {
+    typename Base::KV w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kVe / 4; ++j)
+        fp8x4_to_bf16(kv.v[i][j], &w.v[i].w[2 * j], &w.v[i].w[2 * j + 1]);
+    return Base::build_v(w);
+  }
+  __device__ static void pv(f32x4 (&o)[Base::kChunks], const KV& kv, P p) {
+    Base::pv_with(o, build_v(kv), p);
+  }
+};
 
 // fp32 storage: QK and PV with 16x16x4 (one element per lane per MFMA).
 template <int D>
 struct Ops<F32, D> {
   static_assert(D == 64 || D == 128, "head_dim");
   using storage = float;
+  using kv_storage = float;
   static constexpr int kKv = D / 16;   // 4-float K vectors per lane
   static constexpr int kVe = D / 16;   // V elements per (lane, key)
   static constexpr int kChunks = D / 16;
@@ -548,11 +646,11 @@ __device__ inline void consume_block_tiles(RowState<D> (&st)[RT], const typename
 // every wave of the workgroup must then run the same number of blocks.
 template <class E, int D, int DEPTH, bool SYNC = false>
 __device__ inline void stream_blocks(RowState<D>& st, const typename Ops<E, D>::Q& q,
-                                     const KvView<typename Ops<E, D>::storage>& kv_view,
+                                     const KvView<typename Ops<E, D>::kv_storage>& kv_view,
                                      int b_begin, int n, int key_end, int seq_len,
                                      float scale_log2, int lane) {
   using O = Ops<E, D>;
-  using S = typename O::storage;
+  using S = typename O::kv_storage;
   using KV = typename O::KV;
   if (n <= 0) return;
   const typename O::Off off = O::offsets(kv_view.rs, lane);

@@ -204,9 +204,10 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     const int key_end = !row_valid ? 0 : (a.causal ? min(ctx + tok + 1, seq_len) : seq_len);
     const int kvh = hg * NW + wave;
 
-    KvView<S> view;
-    view.k = static_cast<const S*>(a.k_cache) + (int64_t)kvh * D;
-    view.v = static_cast<const S*>(a.v_cache) + (int64_t)kvh * D;
+    using KS = typename O::kv_storage;
+    KvView<KS> view;
+    view.k = static_cast<const KS*>(a.k_cache) + (int64_t)kvh * D;
+    view.v = static_cast<const KS*>(a.v_cache) + (int64_t)kvh * D;
     view.rs = (int64_t)hkv * D;
     view.table = a.block_table + (int64_t)r * a.max_blocks;
     view.num_blocks = a.num_blocks;
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     const int64_t sg = (int64_t)r * HG + hg;
     const bool whole = b == 0 && len == nb;
     if (row_valid) {
-      const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+      const float inv = (st.l > 0.f ? 1.f / st.l : 0.f) * a.out_scale;
       if (whole) {
         S* dst = static_cast<S*>(a.out) + (qrow * a.num_heads + head) * D + (D / 4) * grp;
 #pragma unroll
@@ -408,6 +409,7 @@ int balanced_total_waves(pa_dtype dtype, int head_dim, int num_kv_heads) {
     case PA_BF16: per_cu = head_dim == 128 ? occupancy_waves<Bf16, 128>(nw) : occupancy_waves<Bf16, 64>(nw); break;
     case PA_F16: per_cu = head_dim == 128 ? occupancy_waves<F16, 128>(nw) : occupancy_waves<F16, 64>(nw); break;
     case PA_F32: per_cu = head_dim == 128 ? occupancy_waves<F32, 128>(nw) : occupancy_waves<F32, 64>(nw); break;
+    case PA_FP8_E4M3: per_cu = head_dim == 128 ? occupancy_waves<Fp8, 128>(nw) : occupancy_waves<Fp8, 64>(nw); break;
   }
   return per_cu * cus;
 }
@@ -420,6 +422,7 @@ hipError_t launch_balanced(const BalancedArgs& a, pa_dtype dtype, hipStream_t st
     case PA_BF16: return d == 128 ? launch_nw<Bf16, 128>(a, nw, stream) : launch_nw<Bf16, 64>(a, nw, stream);
     case PA_F16: return d == 128 ? launch_nw<F16, 128>(a, nw, stream) : launch_nw<F16, 64>(a, nw, stream);
     case PA_F32: return d == 128 ? launch_nw<F32, 128>(a, nw, stream) : launch_nw<F32, 64>(a, nw, stream);
+    case PA_FP8_E4M3: return d == 128 ? launch_nw<Fp8, 128>(a, nw, stream) : launch_nw<Fp8, 64>(a, nw, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -14,15 +14,30 @@ using pa::AttnArgs;
 constexpr int kSupportedBlock = 16;
 constexpr int kMaxGroup = 16;
 
-bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+bool dtype_ok(pa_dtype d) {
+  return d == PA_F32 || d == PA_F16 || d == PA_BF16 || d == PA_FP8_E4M3;
+}
+// bytes of one cache element, and of one query / new-row / output element
+int kv_bytes(pa_dtype d) { return d == PA_F32 ? 4 : d == PA_FP8_E4M3 ? 1 : 2; }
+int act_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
 
 pa_status check_cache(const pa_kv_cache* c) {
   if (c == nullptr || c->k_cache == nullptr || c->v_cache == nullptr) return PA_ERR_NULL;
   if (!dtype_ok(c->dtype)) return PA_ERR_DTYPE;
   if (c->num_blocks <= 0 || c->block_size <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
     return PA_ERR_SHAPE;
+  if (c->dtype == PA_FP8_E4M3 &&
+      !(isfinite(c->k_scale) && c->k_scale > 0.f && isfinite(c->v_scale) && c->v_scale > 0.f))
+    return PA_ERR_SHAPE;
   return PA_OK;
 }
+
+// softmax scale in log2 units, with an E4M3 cache's K scale folded in
+float scale_log2_of(const pa_kv_cache* c, float scale) {
+  const double k = c->dtype == PA_FP8_E4M3 ? (double)c->k_scale : 1.0;
+  return (float)((double)scale * k * 1.4426950408889634);
+}
+float out_scale_of(const pa_kv_cache* c) { return c->dtype == PA_FP8_E4M3 ? c->v_scale : 1.0f; }
 
 pa_status check_attention_shape(const pa_kv_cache* c, int num_seqs, int num_heads,
                                 int max_blocks_per_seq, int max_seq_len, float scale) {
@@ -56,7 +71,8 @@ AttnArgs base_args(const pa_kv_cache* c, const void* q, const int32_t* block_tab
   a.max_blocks = max_blocks_per_seq;
   a.num_splits = 1;
   a.num_tiles = 1;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = scale_log2_of(c, scale);
+  a.out_scale = out_scale_of(c);
   a.causal = 1;
   a.pf_splits = 1;  // prefill tiles unsplit unless a workspace holds partials
   a.pf_split_blocks = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
@@ -78,7 +94,7 @@ int decode_waves(int blocks) {
 // waves per workgroup): the value depends only on the compiled kernel and the
 // device.
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_total_waves[kMaxDevices][3][2][4];
+std::atomic<int> g_total_waves[kMaxDevices][4][2][4];
 struct TotalWavesInit {
   TotalWavesInit() {
     for (auto& d : g_total_waves)
@@ -174,8 +190,8 @@ pa_status pa_write_kv(const pa_kv_cache* cache, const void* k_new, const void* v
   if (num_tokens < 0) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
-  const int elem = cache->dtype == PA_F32 ? 4 : 2;
-  if (((int64_t)cache->num_kv_heads * cache->head_dim * elem) % 16 != 0)
+  if (((int64_t)cache->num_kv_heads * cache->head_dim * act_bytes(cache->dtype)) % 16 != 0 ||
+      ((int64_t)cache->num_kv_heads * cache->head_dim * kv_bytes(cache->dtype)) % 8 != 0)
     return PA_ERR_UNSUPPORTED;
   return launched(pa::launch_write_kv(cache, k_new, v_new, slot_mapping, num_tokens,
                                       static_cast<hipStream_t>(stream)));
@@ -191,6 +207,7 @@ pa_status pa_rope_write_kv(const pa_kv_cache* cache, void* q, int num_heads, con
   if (rotary_dim < 2 || rotary_dim % 2 != 0 || rotary_dim > cache->head_dim) return PA_ERR_SHAPE;
   if (neox_style != 0 && neox_style != 1) return PA_ERR_SHAPE;
   if (num_heads % cache->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (cache->dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
   if (q == nullptr || k_new == nullptr || v_new == nullptr || slot_mapping == nullptr ||
       positions == nullptr || cos_sin == nullptr)
@@ -271,7 +288,7 @@ pa_status pa_decode_splitk(const pa_kv_cache* cache, float* o_part, float* lse_p
 pa_status pa_lse_merge(void* out, float* lse_out, const float* o_part, const float* lse_part,
                        const int32_t* seq_lens, int num_seqs, int num_heads, int head_dim,
                        int max_seq_len, int split_tokens, pa_dtype out_dtype, void* stream) {
-  if (!dtype_ok(out_dtype)) return PA_ERR_DTYPE;
+  if (!dtype_ok(out_dtype) || out_dtype == PA_FP8_E4M3) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len < 0) return PA_ERR_SHAPE;
   if (split_tokens <= 0) return PA_ERR_WORKSPACE;
   if (num_seqs == 0) return PA_OK;
@@ -343,6 +360,7 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
   // prefill chunks (query rows x group > 16): the LDS-staged prefill kernel,
   // long tiles cut into KV splits when the workspace holds their partials
   if ((int64_t)max_query_len * a.group > 16) {
+    if (cache->dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
     const int tt = pa::prefill_tile_tokens(cache->dtype, a.group);
     a.num_tiles = (max_query_len + tt - 1) / tt;
     if (use_ws && vl.pf_splits > 1) {
@@ -387,6 +405,7 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
     b.max_blocks = max_blocks_per_seq;
     b.total_waves = tw;
     b.scale_log2 = a.scale_log2;
+    b.out_scale = a.out_scale;
     return launched(pa::launch_balanced(b, cache->dtype, st));
   }
   a.num_tiles = 1;
@@ -453,7 +472,8 @@ pa_status pa_decode_balanced(const pa_kv_cache* cache, void* out, const void* q,
   a.num_blocks = cache->num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.total_waves = tw;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = scale_log2_of(cache, scale);
+  a.out_scale = out_scale_of(cache);
   return launched(pa::launch_balanced(a, cache->dtype, static_cast<hipStream_t>(stream)));
 }
 

@@ -29,7 +29,8 @@ struct AttnArgs {
   int num_splits;            // S (1 unless writing partials)
   int split_blocks;          // KV blocks per split
   int num_tiles;             // query tiles per request (varlen)
-  float scale_log2;          // scale * log2(e)
+  float scale_log2;          // scale * log2(e) (times the K scale of an E4M3 cache)
+  float out_scale;           // output factor: the V scale of an E4M3 cache, else 1
   int causal;
   // Prefill KV splits: a prefill tile whose keys span more than
   // pf_split_blocks blocks is processed as several splits that write
@@ -95,7 +96,8 @@ struct BalancedArgs {
   int num_blocks;
   int max_blocks;
   int total_waves;
-  float scale_log2;
+  float scale_log2;          // scale * log2(e) (times the K scale of an E4M3 cache)
+  float out_scale;           // output factor: the V scale of an E4M3 cache, else 1
 };
 
 // Waves per workgroup the attention kernel is built for.

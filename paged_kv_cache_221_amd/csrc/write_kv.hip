@@ -36,6 +36,56 @@ __global__ __launch_bounds__(kWriteThreads) void write_kv_kernel(
   }
 }
 
+// E4M3 code of an fp32 value: the nearest of the 8-bit float's values, ties
+// to the even code, magnitudes of 448 (the largest finite value) and more
+// saturating to 448, NaN kept (0x7f with the sign). Integer operations on the
+// fp32 bits: a normal result keeps 3 mantissa bits (a carry moves into the
+// exponent); below 2^-6 the values are the multiples of 2^-9.
+__device__ inline unsigned e4m3_code(float y) {
+  const unsigned u = __float_as_uint(y);
+  const unsigned sign = (u >> 24) & 0x80u;
+  const unsigned au = u & 0x7fffffffu;
+  if (au > 0x7f800000u) return sign | 0x7fu;
+  const float ay = __uint_as_float(au);
+  if (!(ay < 448.0f)) return sign | 0x7eu;
+  if (ay < 0.015625f) return sign | (unsigned)__builtin_rintf(ay * 512.0f);
+  const unsigned e = (au >> 23) - 120u;  // biased E4M3 exponent, 1 .. 15
+  const unsigned mant = au & 0x7fffffu;
+  unsigned r = mant >> 20;
+  const unsigned rem = mant & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+  return sign | min((e << 3) + r, 0x7eu);
+}
+
+// KV write into an E4M3 cache: bf16 rows in, each element divided by the
+// cache's scale (fp32, correctly rounded) and stored as its E4M3 code. Each
+// thread converts 8 elements (16 bytes in, 8 bytes out).
+__global__ __launch_bounds__(kWriteThreads) void write_kv_fp8_kernel(
+    const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
+    u32x2* __restrict__ k_cache, u32x2* __restrict__ v_cache,
+    const int64_t* __restrict__ slot_mapping, int groups_per_row, int64_t num_slots,
+    float k_scale, float v_scale) {
+  const int64_t t = blockIdx.x;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  for (int i = threadIdx.x; i < 2 * groups_per_row; i += kWriteThreads) {
+    const bool is_k = i < groups_per_row;
+    const int gidx = is_k ? i : i - groups_per_row;
+    const u32x4 x = (is_k ? k_new : v_new)[t * groups_per_row + gidx];
+    const float sc = is_k ? k_scale : v_scale;
+    const unsigned w[4] = {x.x, x.y, x.z, x.w};
+    unsigned c[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[2 * j] = e4m3_code(__fdiv_rn(__uint_as_float(w[j] << 16), sc));
+      c[2 * j + 1] = e4m3_code(__fdiv_rn(__uint_as_float(w[j] & 0xffff0000u), sc));
+    }
+    const u32x2 out = {c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                       c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+    (is_k ? k_cache : v_cache)[slot * groups_per_row + gidx] = out;
+  }
+}
+
 __global__ __launch_bounds__(kWriteThreads) void copy_blocks_kernel(
     u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, const int32_t* __restrict__ src_dst,
     int64_t vecs_per_block, int num_blocks) {
@@ -178,7 +228,7 @@ hipError_t launch_rope_write_kv(const pa_kv_cache* c, void* q, int num_heads, co
 hipError_t launch_copy_blocks(const pa_kv_cache* c, const int32_t* src_dst, int num_pairs,
                               hipStream_t stream) {
   if (num_pairs <= 0) return hipSuccess;
-  const int elem = c->dtype == PA_F32 ? 4 : 2;
+  const int elem = c->dtype == PA_F32 ? 4 : c->dtype == PA_FP8_E4M3 ? 1 : 2;
   const int64_t block_bytes = (int64_t)c->block_size * c->num_kv_heads * c->head_dim * elem;
   copy_blocks_kernel<<<dim3((unsigned)num_pairs), dim3(kWriteThreads), 0, stream>>>(
       static_cast<u32x4*>(c->k_cache), static_cast<u32x4*>(c->v_cache), src_dst, block_bytes / 16,
@@ -189,6 +239,14 @@ hipError_t launch_copy_blocks(const pa_kv_cache* c, const int32_t* src_dst, int 
 hipError_t launch_write_kv(const pa_kv_cache* c, const void* k_new, const void* v_new,
                            const int64_t* slot_mapping, int num_tokens, hipStream_t stream) {
   if (num_tokens <= 0) return hipSuccess;
+  if (c->dtype == PA_FP8_E4M3) {
+    const int groups = c->num_kv_heads * c->head_dim / 8;
+    write_kv_fp8_kernel<<<dim3((unsigned)num_tokens), dim3(kWriteThreads), 0, stream>>>(
+        static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new),
+        static_cast<u32x2*>(c->k_cache), static_cast<u32x2*>(c->v_cache), slot_mapping, groups,
+        (int64_t)c->num_blocks * c->block_size, c->k_scale, c->v_scale);
+    return hipGetLastError();
+  }
   const int elem = c->dtype == PA_F32 ? 4 : 2;
   const int64_t row_bytes = (int64_t)c->num_kv_heads * c->head_dim * elem;
   const int vecs_per_row = (int)(row_bytes / 16);

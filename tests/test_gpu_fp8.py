@@ -1,0 +1,181 @@
+"""GPU parity of the E4M3 (8-bit float) KV cache against the oracle.
+
+The quantising write must match the oracle's codes bit for bit (both divide
+in fp32, then round to the nearest E4M3 value, ties to even, saturating).
+Attention reads codes, widens them exactly to bf16 MFMA operands and applies
+the K scale inside the softmax scale and the V scale to the output; against
+the fp64 oracle over the dequantised values the error is the bf16 path's
+(bf16 probabilities, fp32 sums), so the bf16 bound 2e-2 applies.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_221_amd as pa
+from oracle import fp8
+from oracle.block_manager import copy_blocks
+from workloads import small_decode, small_varlen
+from workloads.tensors import materialize_e4m3, raw_bits
+
+from _parity import max_err, gpu_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+class _Fp8Step:
+    """E4M3 caches on the GPU plus host copies of every input bit."""
+
+    def __init__(self, layout, k_scale, v_scale):
+        self.lay = layout
+        self.ks, self.vs = k_scale, v_scale
+        self.st = materialize_e4m3(layout, "cuda", k_scale, v_scale)
+        self.k = raw_bits(self.st.k_cache, "e4m3").copy()
+        self.v = raw_bits(self.st.v_cache, "e4m3").copy()
+        self.q = raw_bits(self.st.q, "bf16")
+        self.k_new = raw_bits(self.st.k_new, "bf16")
+        self.v_new = raw_bits(self.st.v_new, "bf16")
+
+    def write(self):
+        st, lay = self.st, self.lay
+        pa.pa_write_kv(st.k_cache, st.v_cache, st.k_new, st.v_new, st.slot_mapping,
+                       k_scale=self.ks, v_scale=self.vs)
+        fp8.write_kv(self.k, self.v, self.k_new, self.v_new, lay.slot_mapping, lay.block_size,
+                     self.ks, self.vs)
+        torch.cuda.synchronize()
+        assert np.array_equal(raw_bits(st.k_cache, "e4m3"), self.k), "K codes differ"
+        assert np.array_equal(raw_bits(st.v_cache, "e4m3"), self.v), "V codes differ"
+
+    def kw(self):
+        return dict(k_scale=self.ks, v_scale=self.vs)
+
+    def decode_oracle(self, requests=None):
+        lay = self.lay
+        return oracle.paged_decode(self.q, self.k, self.v, lay.block_table, lay.seq_lens,
+                                   lay.scale, lay.block_size, "bf16", requests=requests,
+                                   kv_dtype="e4m3", k_scale=self.ks, v_scale=self.vs)
+
+
+def test_fp8_write_bit_exact_with_special_values(gpu_lib):
+    lay = small_varlen(81, dtype="bf16", head_dim=64, num_heads=8, num_kv_heads=4)
+    s = _Fp8Step(lay, 0.0625, 0.02)
+    kn = s.st.k_new.view(torch.int16)
+    kn[0, 0, :4] = torch.tensor([0x7FC1, -32768, 0x7F80, -128], dtype=torch.int16)  # NaN, -0, +inf, -inf
+    s.st.k_new[1, 0, :8] = torch.tensor([1e4, -1e4, 28.0, 28.001, 1e-6, -1e-6, 3e-4, 448 * 0.0625],
+                                        dtype=torch.bfloat16)
+    s.st.v_new[2, 3, :] = 0.02 * 0.5 * (1 + 1 / 8)    # halfway between two codes before rounding
+    s.st.slot_mapping[5] = -1                          # a padding token
+    lay.slot_mapping = lay.slot_mapping.copy()
+    lay.slot_mapping[5] = -1
+    s.k_new = raw_bits(s.st.k_new, "bf16")
+    s.v_new = raw_bits(s.st.v_new, "bf16")
+    s.write()
+
+
+FP8_DECODE = [(128, 32, 8, 7, 700), (64, 8, 2, 9, 400), (128, 16, 1, 5, 1200),
+              (128, 8, 8, 4, 33)]
+
+
+@pytest.mark.parametrize("case", FP8_DECODE, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("kernel", ["decode", "balanced"])
+def test_fp8_decode_parity(gpu_lib, case, kernel):
+    d, hq, hkv, batch, max_len = case
+    lay = small_decode(900 + d + hq + batch, dtype="bf16", batch=batch, min_len=1,
+                       max_len=max_len, num_heads=hq, num_kv_heads=hkv, head_dim=d)
+    s = _Fp8Step(lay, 0.0625, 0.125 / 3)
+    s.write()
+    st = s.st
+    fn = pa.pa_decode if kernel == "decode" else pa.pa_decode_balanced
+    out = fn(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens, lay.max_seq_len,
+             lay.scale, **s.kw())
+    torch.cuda.synchronize()
+    want, _ = s.decode_oracle()
+    err = max_err(gpu_rows(out, "bf16"), want)
+    print(f"{lay.name} e4m3 {kernel}: max|err| = {err:.3e}", flush=True)
+    assert out.dtype == torch.bfloat16 and err <= TOL
+
+
+@pytest.mark.parametrize("split", [32, 160])
+def test_fp8_splitk_and_merge(gpu_lib, split):
+    lay = small_decode(950 + split, dtype="bf16", batch=6, min_len=1, max_len=600,
+                       num_heads=8, num_kv_heads=2, head_dim=128, key_outlier_frac=0.05)
+    s = _Fp8Step(lay, 0.05, 0.03)
+    s.write()
+    st = s.st
+    o_part, lse_part = pa.pa_decode_splitk(st.k_cache, st.v_cache, st.q, st.block_table,
+                                           st.seq_lens, lay.max_seq_len, split, lay.scale,
+                                           **s.kw())
+    out, lse = pa.pa_lse_merge(o_part, lse_part, st.seq_lens, lay.max_seq_len, split,
+                               out_dtype=torch.bfloat16, want_lse=True)
+    torch.cuda.synchronize()
+    want_o, want_l = oracle.splitk_partials(s.q, s.k, s.v, lay.block_table, lay.seq_lens,
+                                            lay.scale, lay.block_size, "bf16", split,
+                                            o_part.shape[2], kv_dtype="e4m3", k_scale=s.ks,
+                                            v_scale=s.vs)
+    got_l = lse_part.cpu().double().numpy()
+    empty = np.isneginf(want_l)
+    assert np.array_equal(np.isneginf(got_l), empty)
+    assert max_err(o_part.cpu().double().numpy()[~empty], want_o[~empty]) <= TOL
+    assert max_err(got_l[~empty], want_l[~empty]) <= TOL
+    want, want_lse = s.decode_oracle()
+    assert max_err(gpu_rows(out, "bf16"), want) <= TOL
+    assert max_err(lse.cpu().double().numpy(), want_lse) <= TOL
+
+
+@pytest.mark.parametrize("path", ["balanced", "direct"])
+def test_fp8_varlen_decode_and_short_queries(gpu_lib, path):
+    """Decode rows and multi-token queries that fit one 16-row tile (group 4:
+    up to 4 tokens), causal, through both single-tile paths."""
+    lay = small_varlen(970, dtype="bf16", num_heads=16, num_kv_heads=4, head_dim=128,
+                       prefill=((3, 60), (2, 0), (4, 100), (4, 13)),
+                       decode_lens=(1, 15, 16, 17, 300))
+    s = _Fp8Step(lay, 0.0625, 0.04)
+    s.write()
+    st = s.st
+    out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
+                       workspace="auto" if path == "balanced" else None, **s.kw())
+    torch.cuda.synchronize()
+    want, _ = oracle.paged_varlen(s.q, s.k, s.v, lay.cu_seqlens_q, lay.seq_lens,
+                                  lay.block_table, lay.scale, lay.block_size, "bf16",
+                                  kv_dtype="e4m3", k_scale=s.ks, v_scale=s.vs)
+    err = max_err(gpu_rows(out, "bf16"), want)
+    print(f"{lay.name} e4m3 varlen {path}: max|err| = {err:.3e}", flush=True)
+    assert err <= TOL
+
+
+def test_fp8_prefill_and_rope_are_refused(gpu_lib):
+    lay = small_varlen(975, dtype="bf16", num_heads=8, num_kv_heads=2, head_dim=128,
+                       prefill=((40, 0),), decode_lens=(5,))
+    s = _Fp8Step(lay, 0.1, 0.1)
+    st = s.st
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                     st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale, **s.kw())
+    assert e.value.status == -4
+    cos_sin = torch.ones((64, 128), dtype=torch.float32, device="cuda")
+    pos = torch.zeros(st.q.shape[0], dtype=torch.int32, device="cuda")
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_rope_write_kv(st.k_cache, st.v_cache, st.q, st.k_new, st.v_new, st.slot_mapping,
+                            pos, cos_sin, 128)
+    assert e.value.status == -4
+
+
+def test_fp8_copy_blocks_bit_exact(gpu_lib):
+    lay = small_decode(980, dtype="bf16", batch=4, min_len=20, max_len=200, num_heads=8,
+                       num_kv_heads=2, head_dim=64)
+    s = _Fp8Step(lay, 0.05, 0.05)
+    st = s.st
+    nb = lay.num_blocks
+    rng = np.random.Generator(np.random.PCG64(981))
+    src = rng.choice(nb, size=6, replace=False)
+    dst = rng.choice(np.setdiff1d(np.arange(nb), src), size=6, replace=False)
+    pairs = np.stack([src, dst], axis=1).astype(np.int32)
+    pa.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    want_k, want_v = copy_blocks(s.k, s.v, [tuple(p) for p in pairs.tolist()])
+    assert np.array_equal(raw_bits(st.k_cache, "e4m3"), want_k)
+    assert np.array_equal(raw_bits(st.v_cache, "e4m3"), want_v)

@@ -25,8 +25,8 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
-def _cache(nb=8, bs=16, hkv=2, d=128, dtype=2, k=1, v=1):
-    return _native.PaKvCache(k, v, nb, bs, hkv, d, dtype)
+def _cache(nb=8, bs=16, hkv=2, d=128, dtype=2, k=1, v=1, ks=1.0, vs=1.0):
+    return _native.PaKvCache(k, v, nb, bs, hkv, d, dtype, ks, vs)
 
 
 def test_status_strings(lib):
@@ -102,3 +102,25 @@ def test_balanced_validation_codes(lib):
                                   one, 1 << 30, None) == -4
     assert lib.pa_decode_balanced_workspace_bytes(None, 4, 8) == 0
     assert lib.pa_decode_balanced_workspace_bytes(byref(_cache()), 4, 7) == 0
+
+
+def test_e4m3_cache_validation(lib):
+    """An E4M3 cache (dtype 3) needs finite positive scales; its prefill
+    tiles, the fused RoPE write and an E4M3 merge output are not offered."""
+    byref = ctypes.byref
+    one = ctypes.c_void_p(1)
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("nan"), 1.0), (1.0, float("inf"))):
+        c = _cache(dtype=3, ks=ks, vs=vs)
+        assert lib.pa_decode(byref(c), one, one, one, one, 1, 8, 4, 64, 0.1, None) == -2
+        assert lib.pa_write_kv(byref(c), one, one, one, 4, None) == -2
+    # other dtypes ignore the scale fields
+    assert lib.pa_decode(byref(_cache(ks=0.0, vs=float("nan"))), None, None, None, None, 0, 8,
+                         4, 64, 0.1, None) == 0
+    c = _cache(dtype=3, ks=0.05, vs=0.02)
+    assert lib.pa_decode(byref(c), None, None, None, None, 0, 8, 4, 64, 0.1, None) == 0
+    # 40 query rows x group 4 > one 16-row tile: a prefill chunk
+    assert lib.pa_varlen(byref(c), one, one, one, one, one, 1, 40, 8, 4, 40, 64, 0.1, 1,
+                         None, 0, None) == -4
+    assert lib.pa_rope_write_kv(byref(c), one, 8, one, one, one, one, one, 128, 128, 1, 4,
+                                None) == -4
+    assert lib.pa_lse_merge(one, None, one, one, one, 1, 8, 128, 64, 32, 3, None) == -3

@@ -27,9 +27,10 @@ import torch
 
 from .layout import StepLayout
 
-TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-RAW_DTYPES = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16}
-NP_RAW = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+                "e4m3": torch.float8_e4m3fn}
+RAW_DTYPES = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16, "e4m3": torch.uint8}
+NP_RAW = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
 
 _CHUNK_ELEMS = 1 << 26   # fp32 temporaries of at most 256 MiB
 
@@ -111,6 +112,31 @@ def materialize(layout: StepLayout, device, *, poison: bool = True,
         seq_lens=torch.from_numpy(layout.seq_lens).to(dev),
         cu_seqlens_q=torch.from_numpy(layout.cu_seqlens_q).to(dev),
         slot_mapping=torch.from_numpy(layout.slot_mapping).to(dev))
+
+
+def materialize_e4m3(layout: StepLayout, device, k_scale: float, v_scale: float,
+                     **kw) -> StepTensors:
+    """A bf16 layout's tensors with the two caches held as 8-bit E4M3 floats
+    (OCP "e4m3fn"): each cached element x becomes the E4M3 value of
+    clamp(x / scale, -448, 448) by torch's conversion, NaN poison staying NaN.
+    q and the new K/V rows stay bf16."""
+    if layout.dtype != "bf16":
+        raise ValueError("an E4M3 cache is drawn from a bf16 layout")
+    st = materialize(layout, device, **kw)
+    f8 = torch.float8_e4m3fn
+
+    def conv(c, scale):
+        out = torch.empty(c.shape, dtype=f8, device=c.device)
+        rows_in, rows_out = c.view(c.shape[0], -1), out.view(c.shape[0], -1)
+        step = max(1, _CHUNK_ELEMS // max(1, rows_in.shape[1]))
+        for lo in range(0, rows_in.shape[0], step):
+            x = rows_in[lo:lo + step].float().div_(scale)
+            rows_out[lo:lo + step] = torch.where(x.isnan(), x, x.clamp(-448.0, 448.0)).to(f8)
+        return out
+
+    st.k_cache = conv(st.k_cache, k_scale)
+    st.v_cache = conv(st.v_cache, v_scale)
+    return st
 
 
 def raw_bits(x: torch.Tensor, dtype: str) -> np.ndarray:
