@@ -297,6 +297,12 @@ struct Ops<F16, D> : Ops16<F16, D> {
 // E4M3 cache: the bf16 tile with half-size loads. The registers keep the raw
 // codes until the block is consumed (so loads stay in flight); scores() and
 // build_v() widen them to the bf16 operands of Ops16<Bf16, D>.
+//
+// The QK product sums over head_dim in any order as long as K and Q agree, so
+// K is read in 16-byte pieces: lane (m, grp) loads bytes 16*(grp + 4j) .. +15
+// of key row m for j < D/64, whose two 8-byte halves are the lane's slots of
+// QK chunks 2j and 2j+1. load_q reads q with the same assignment. V keeps the
+// bf16 layout (one 128-byte key row per 16 lanes and load).
 template <int D>
 struct Ops<Fp8, D> : Ops16<Bf16, D> {
   using Base = Ops16<Bf16, D>;
@@ -305,27 +311,30 @@ struct Ops<Fp8, D> : Ops16<Bf16, D> {
   using typename Base::P;
   using typename Base::VA;
   static constexpr int kQk = D / 32;
+  static constexpr int kK16 = D / 64;  // 16-byte K loads per lane
   static constexpr int kVe = D / 16;
   struct KV {
-    u32x2 k[kQk];            // 8 codes per 32-dim chunk
+    u32x4 k[kK16];
     unsigned v[4][kVe / 4];  // kVe codes of each of the lane's four key rows
   };
   struct Off {
-    int k[kQk];
+    int k[kK16];
     int v[4];
   };
+  // head_dim index of the first of the 8 elements lane group grp holds in QK chunk c
+  __device__ static int qk_dim(int c, int grp) { return 16 * (grp + 4 * (c >> 1)) + 8 * (c & 1); }
   __device__ static Off offsets(int64_t rs, int lane) {
     const int m = lane & 15, grp = lane >> 4;
     Off o;
 #pragma unroll
-    for (int c = 0; c < kQk; ++c) o.k[c] = (int)(m * rs + 32 * c + 8 * grp);
+    for (int j = 0; j < kK16; ++j) o.k[j] = (int)(m * rs + 16 * (grp + 4 * j));
 #pragma unroll
     for (int i = 0; i < 4; ++i) o.v[i] = (int)((4 * grp + i) * rs + kVe * m);
     return o;
   }
   __device__ static void load(KV& kv, Rsrc kr, Rsrc vr, const Off& o) {
 #pragma unroll
-    for (int c = 0; c < kQk; ++c) kv.k[c] = buf_load8(kr, o.k[c]);
+    for (int j = 0; j < kK16; ++j) kv.k[j] = buf_load16(kr, o.k[j]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (kVe == 8) {
@@ -337,13 +346,22 @@ struct Ops<Fp8, D> : Ops16<Bf16, D> {
       }
     }
   }
+  __device__ static void load_q(Q& q, const uint16_t* qrow, bool valid, int lane) {
+    const int grp = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < kQk; ++c) {
+      q.q[c] = valid ? *reinterpret_cast<const u32x4*>(qrow + qk_dim(c, grp))
+                     : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   __device__ static f32x4 scores(const KV& kv, const Q& q) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < kQk; ++c) {
+      const u32x4& w = kv.k[c >> 1];
       unsigned w0, w1, w2, w3;
-      fp8x4_to_bf16(kv.k[c].x, &w0, &w1);
-      fp8x4_to_bf16(kv.k[c].y, &w2, &w3);
+      fp8x4_to_bf16((c & 1) ? w.z : w.x, &w0, &w1);
+      fp8x4_to_bf16((c & 1) ? w.w : w.y, &w2, &w3);
       acc = Bf16::mma_qk(u32x4{w0, w1, w2, w3}, q.q[c], acc);
     }
     return acc;
@@ -502,13 +520,19 @@ __device__ inline void store_chunk(typename Ops<E, D>::storage* dst, const float
 }
 
 // KV blocks each wave keeps in flight. fp32 operands are twice the size, so
-// they get half the depth to stay within the register budget.
+// they get half the depth to stay within the register budget; E4M3 blocks
+// are half the size and get their own.
 #ifndef PA_KV_DEPTH
 #define PA_KV_DEPTH 4
 #endif
+#ifndef PA_KV_FP8_DEPTH
+#define PA_KV_FP8_DEPTH 4
+#endif
 template <class E>
 constexpr int kv_depth() {
-  return sizeof(typename E::storage) == 4 ? 2 : PA_KV_DEPTH;
+  return sizeof(typename E::kv_storage) == 4   ? 2
+         : sizeof(typename E::kv_storage) == 1 ? PA_KV_FP8_DEPTH
+                                               : PA_KV_DEPTH;
 }
 
 // ------------------------------------------------------------ row tile state

@@ -31,12 +31,16 @@ namespace pa {
 namespace {
 
 // Waves per SIMD the kernel is built for and KV blocks each wave keeps in
-// flight (compile-time tunables; fp32 operands get half the depth).
+// flight (compile-time tunables; fp32 operands get half the depth, an E4M3
+// cache, whose blocks are half the bytes, its own).
 #ifndef PA_BAL_OCC
 #define PA_BAL_OCC 2
 #endif
 #ifndef PA_BAL_DEPTH
 #define PA_BAL_DEPTH 2
+#endif
+#ifndef PA_BAL_FP8_DEPTH
+#define PA_BAL_FP8_DEPTH 3
 #endif
 // Whether the head waves of a workgroup meet at a barrier every DEPTH blocks.
 #ifndef PA_BAL_SYNC
@@ -44,7 +48,9 @@ namespace {
 #endif
 template <class E>
 constexpr int bal_depth() {
-  return sizeof(typename E::storage) == 4 ? (PA_BAL_DEPTH + 1) / 2 : PA_BAL_DEPTH;
+  return sizeof(typename E::kv_storage) == 4   ? (PA_BAL_DEPTH + 1) / 2
+         : sizeof(typename E::kv_storage) == 1 ? PA_BAL_FP8_DEPTH
+                                               : PA_BAL_DEPTH;
 }
 
 // Exclusive prefix sum over the workgroup; *total gets the sum of all v.

@@ -199,6 +199,113 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_kv_kernel(
   for (int64_t i = threadIdx.x; i < row_elems; i += kWriteThreads) vd[i] = vs[i];
 }
 
+// N consecutive floats from an address aligned to 4N bytes (N = 2, 4 or 8).
+template <int N>
+__device__ inline void load_floats(const float* p, float (&out)[N]) {
+  if constexpr (N == 2) {
+    const float2 x = *reinterpret_cast<const float2*>(p);
+    out[0] = x.x;
+    out[1] = x.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(p + i);
+      out[i] = x.x;
+      out[i + 1] = x.y;
+      out[i + 2] = x.z;
+      out[i + 3] = x.w;
+    }
+  }
+}
+
+// The same step in 16-byte vectors (V = 16 / element size elements), for
+// rotary_dim a multiple of 16 and 16-byte aligned rows: a NeoX unit is the V
+// pairs (i, i + rotary_dim/2) for i in [V u, V u + V), two vectors; a GPT-J
+// unit is the V/2 adjacent pairs of one vector. Dimensions past rotary_dim of
+// K and all of V are copied as vectors; q's stay in place.
+template <class E, bool NEOX>
+__global__ __launch_bounds__(kWriteThreads) void rope_write_kv_vec_kernel(
+    typename E::storage* __restrict__ q, const typename E::storage* __restrict__ k_new,
+    const typename E::storage* __restrict__ v_new, typename E::storage* __restrict__ k_cache,
+    typename E::storage* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping,
+    const int32_t* __restrict__ positions, const float* __restrict__ cos_sin, int max_position,
+    int rotary_dim, int num_heads, int num_kv_heads, int head_dim, int64_t num_slots) {
+  using S = typename E::storage;
+  constexpr int V = 16 / (int)sizeof(S);
+  constexpr int NP = NEOX ? V : V / 2;  // pairs per unit
+  const int64_t t = blockIdx.x;
+  const int pos = positions[t];
+  if (pos < 0 || pos >= max_position) return;  // outside the table: token left alone
+  const int half = rotary_dim / 2;
+  const int units = NEOX ? half / V : rotary_dim / V;  // rotation units per head row
+  const float* cs = cos_sin + (int64_t)pos * rotary_dim;
+
+  // rotates unit u of the head row src into dst (dst may equal src)
+  auto rotate = [&](const S* src, S* dst, int u) {
+    const int j0 = u * NP;  // first pair of the unit
+    float c[NP], sn[NP];
+    load_floats<NP>(cs + j0, c);
+    load_floats<NP>(cs + half + j0, sn);
+    if constexpr (NEOX) {
+      const u32x4 va = *reinterpret_cast<const u32x4*>(src + V * u);
+      const u32x4 vb = *reinterpret_cast<const u32x4*>(src + V * u + half);
+      S a[V], b[V];
+      __builtin_memcpy(a, &va, 16);
+      __builtin_memcpy(b, &vb, 16);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float fa = to_f32<E>(a[e]), fb = to_f32<E>(b[e]);
+        a[e] = from_f32<E>(fa * c[e] - fb * sn[e]);
+        b[e] = from_f32<E>(fb * c[e] + fa * sn[e]);
+      }
+      u32x4 oa, ob;
+      __builtin_memcpy(&oa, a, 16);
+      __builtin_memcpy(&ob, b, 16);
+      *reinterpret_cast<u32x4*>(dst + V * u) = oa;
+      *reinterpret_cast<u32x4*>(dst + V * u + half) = ob;
+    } else {
+      const u32x4 vx = *reinterpret_cast<const u32x4*>(src + V * u);
+      S x[V];
+      __builtin_memcpy(x, &vx, 16);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const float fa = to_f32<E>(x[2 * p]), fb = to_f32<E>(x[2 * p + 1]);
+        x[2 * p] = from_f32<E>(fa * c[p] - fb * sn[p]);
+        x[2 * p + 1] = from_f32<E>(fb * c[p] + fa * sn[p]);
+      }
+      u32x4 o;
+      __builtin_memcpy(&o, x, 16);
+      *reinterpret_cast<u32x4*>(dst + V * u) = o;
+    }
+  };
+
+  // queries, in place
+  for (int i = threadIdx.x; i < num_heads * units; i += kWriteThreads) {
+    const int h = i / units;
+    S* row = q + (t * num_heads + h) * head_dim;
+    rotate(row, row, i - h * units);
+  }
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;  // padding token, or outside the pool
+  const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+  const S* ks = k_new + t * row_elems;
+  S* kd = k_cache + slot * row_elems;
+  for (int i = threadIdx.x; i < num_kv_heads * units; i += kWriteThreads) {
+    const int h = i / units;
+    rotate(ks + h * head_dim, kd + h * head_dim, i - h * units);
+  }
+  // K dims past rotary_dim, then all of V, as 16-byte vectors
+  const int rest = (head_dim - rotary_dim) / V;  // vectors per head row
+  for (int i = threadIdx.x; i < num_kv_heads * rest; i += kWriteThreads) {
+    const int h = i / rest;
+    const int64_t e = (int64_t)h * head_dim + rotary_dim + V * (i - h * rest);
+    *reinterpret_cast<u32x4*>(kd + e) = *reinterpret_cast<const u32x4*>(ks + e);
+  }
+  const u32x4* vs = reinterpret_cast<const u32x4*>(v_new + t * row_elems);
+  u32x4* vd = reinterpret_cast<u32x4*>(v_cache + slot * row_elems);
+  for (int64_t i = threadIdx.x; i < row_elems / V; i += kWriteThreads) vd[i] = vs[i];
+}
+
 }  // namespace
 
 hipError_t launch_rope_write_kv(const pa_kv_cache* c, void* q, int num_heads, const void* k_new,
@@ -208,6 +315,34 @@ hipError_t launch_rope_write_kv(const pa_kv_cache* c, void* q, int num_heads, co
   if (num_tokens <= 0) return hipSuccess;
   const int64_t num_slots = (int64_t)c->num_blocks * c->block_size;
   const dim3 grid((unsigned)num_tokens), block(kWriteThreads);
+  auto aligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  const bool vec = rotary_dim % 16 == 0 && c->head_dim % 8 == 0 && aligned(q) &&
+                   aligned(k_new) && aligned(v_new) && aligned(c->k_cache) &&
+                   aligned(c->v_cache) && aligned(cos_sin);
+  if (vec) {
+    switch (c->dtype) {
+#define PA_ROPE_VEC(E)                                                                           \
+  if (neox)                                                                                      \
+    rope_write_kv_vec_kernel<E, true><<<grid, block, 0, stream>>>(                               \
+        static_cast<E::storage*>(q), static_cast<const E::storage*>(k_new),                      \
+        static_cast<const E::storage*>(v_new), static_cast<E::storage*>(c->k_cache),            \
+        static_cast<E::storage*>(c->v_cache), slot_mapping, positions, cos_sin, max_position,    \
+        rotary_dim, num_heads, c->num_kv_heads, c->head_dim, num_slots);                         \
+  else                                                                                           \
+    rope_write_kv_vec_kernel<E, false><<<grid, block, 0, stream>>>(                              \
+        static_cast<E::storage*>(q), static_cast<const E::storage*>(k_new),                      \
+        static_cast<const E::storage*>(v_new), static_cast<E::storage*>(c->k_cache),            \
+        static_cast<E::storage*>(c->v_cache), slot_mapping, positions, cos_sin, max_position,    \
+        rotary_dim, num_heads, c->num_kv_heads, c->head_dim, num_slots);                         \
+  break;
+      case PA_BF16: PA_ROPE_VEC(Bf16)
+      case PA_F16: PA_ROPE_VEC(F16)
+      case PA_F32: PA_ROPE_VEC(F32)
+#undef PA_ROPE_VEC
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (c->dtype) {
 #define PA_ROPE_LAUNCH(E)                                                                        \
   rope_write_kv_kernel<E><<<grid, block, 0, stream>>>(                                          \

@@ -32,8 +32,12 @@ def _bound(x, rotary_dim, neox, dtype):
     return b
 
 
+# rotary_dim a multiple of 16 takes the 16-byte vector kernel, others the
+# element-wise one (40 and 20 below)
 @pytest.mark.parametrize("case", [("bf16", 128, 32, 8, 128, True), ("f16", 64, 8, 2, 32, False),
-                                  ("f32", 128, 16, 4, 64, True), ("bf16", 64, 4, 4, 48, False)],
+                                  ("f32", 128, 16, 4, 64, True), ("bf16", 64, 4, 4, 48, False),
+                                  ("f32", 64, 8, 2, 32, False), ("f16", 128, 8, 2, 40, True),
+                                  ("bf16", 64, 8, 8, 20, False)],
                          ids=lambda c: "-".join(map(str, c)))
 def test_rope_write_kv_parity(gpu_lib, case):
     dtype, d, hq, hkv, rdim, neox = case
