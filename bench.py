@@ -71,6 +71,27 @@ def varlen_bytes(layout) -> int:
     return int(lens.sum() * kvb + qo + 4 * blocks.sum() + 4 * (2 * layout.num_seqs + 1))
 
 
+def causal_flops(layout) -> int:
+    """FLOPs of exact causal attention over a varlen step: query row i of a
+    request with n rows and KV length L sees L - n + i + 1 keys, each costing
+    2 D FLOPs for QK and 2 D for PV, per query head."""
+    pairs = 0
+    for n, length in zip(layout.query_lens.tolist(), layout.seq_lens.tolist()):
+        pairs += n * (length - n) + n * (n + 1) // 2
+    return int(pairs * layout.num_heads * layout.head_dim * 4)
+
+
+def shared_prefix_bytes(layout) -> int:
+    """KV bytes a varlen step reads more than once: every sharer after the
+    first reads the shared prefix blocks again."""
+    sharers = int((layout.block_table[:, :1] == layout.shared_blocks[:1]).sum()) \
+        if len(layout.shared_blocks) else 0
+    kvb = 2 * layout.num_kv_heads * layout.head_dim * layout.elem_bytes
+    return max(sharers - 1, 0) * len(layout.shared_blocks) * layout.block_size * kvb
+
+
+PEAK_BF16_TFLOPS = 2500.0
+
 # Kernels launched by the timed attention call of each path.
 PATH_KERNELS = {
     "decode": "paged_attention_kernel",
@@ -255,14 +276,52 @@ def secondary(args):
                      "attention_GBps": round(nbytes / (kern * 1e-3) / 1e9, 1),
                      "attention_frac_of_8TBps": round(nbytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes": nbytes}
+        if name.startswith("mixed"):
+            uniq = nbytes - shared_prefix_bytes(lay)
+            res[name]["unique_bytes"] = uniq
+            res[name]["attention_unique_GBps"] = round(uniq / (kern * 1e-3) / 1e9, 1)
         print(f"[bench] {name}: attention {kern:.4f} ms", file=sys.stderr, flush=True)
         del st, step
         torch.cuda.empty_cache()
+    res["mixed-step-prefill-chunks-bf16"] = bench_prefill_only(k)
     res["llama3-8b-decode-e4m3-cache"] = bench_fp8_decode(k)
     res["rope-write-kv-mixed-step-bf16"] = bench_rope_write(k)
     res["copy-on-write-blocks-bf16"] = bench_copy_blocks(k)
     res["block-manager-host"] = bench_block_manager()
     return res
+
+
+def bench_prefill_only(k: int):
+    """pa_varlen on the mixed step's 4 prefill chunks alone: the compute rate
+    of the prefill rows, exact causal FLOPs against the bf16 MFMA peak."""
+    import torch
+    import paged_kv_cache_221_amd as pa
+    from workloads import mixed_step_prefill_only
+    from workloads.tensors import materialize
+    lay = mixed_step_prefill_only()
+    st = materialize(lay, "cuda", poison=False)
+    out = torch.empty_like(st.q)
+    ws = torch.empty(pa.pa_varlen_workspace_bytes(st.k_cache, st.v_cache, lay.num_seqs,
+                                                  st.q.shape[0], lay.num_heads,
+                                                  st.block_table.shape[1]),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                     st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale, out=out,
+                     workspace=ws)
+        if ev is not None:
+            ev[1].record()
+    _, kern = time_steps([step], max(k, 10), 3, True)
+    flops = causal_flops(lay)
+    print(f"[bench] prefill chunks: {kern:.4f} ms", file=sys.stderr, flush=True)
+    del st, out, ws
+    torch.cuda.empty_cache()
+    tflops = flops / (kern * 1e-3) / 1e12
+    return {"kernel_ms": round(kern, 4), "flops": flops, "TFLOPs": round(tflops, 1),
+            "frac_of_bf16_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
 def bench_fp8_decode(k: int, copies: int = 4):

@@ -184,9 +184,10 @@ pa_status pa_decode_balanced(const pa_kv_cache *cache, void *out, const void *q,
  * Requests with n_r * group > 16 (prefill chunks) run in a tiled kernel;
  * the others in the balanced kernel of pa_decode_balanced when a workspace is
  * given (partials merged by a further kernel), else one workgroup per
- * (request, KV head). With a workspace, prefill tiles whose keys span more
- * than 512 blocks are also cut into KV splits (at most 8, longer for wider
- * block tables) whose partials a last kernel merges [P1 §07].
+ * (request, KV head). With a workspace, the prefill tiles' KV blocks are also
+ * cut into one equal share per resident workgroup, and the tiles cut between
+ * shares are renormalised by a merge kernel [P1 §07]; without one, each
+ * (tile, request, KV head) gets its own workgroup.
  *   out, q        : [T, Hq, D] in cache->dtype
  *   cu_seqlens_q  : int32 [B + 1], cu[0] = 0, non-decreasing, cu[B] = T
  *   seq_lens      : int32 [B]; KV length including this step's n_r tokens

@@ -74,8 +74,7 @@ AttnArgs base_args(const pa_kv_cache* c, const void* q, const int32_t* block_tab
   a.scale_log2 = scale_log2_of(c, scale);
   a.out_scale = out_scale_of(c);
   a.causal = 1;
-  a.pf_splits = 1;  // prefill tiles unsplit unless a workspace holds partials
-  a.pf_split_blocks = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
+  a.pf_shares = 0;  // prefill: one workgroup per tile unless a workspace holds partials
   return a;
 }
 
@@ -119,6 +118,31 @@ int total_waves(pa_dtype dtype, int head_dim, int num_kv_heads) {
   return v;
 }
 
+// Resident workgroups of the equal-share prefill kernel, cached per
+// (device, dtype, head_dim) like total_waves.
+std::atomic<int> g_pf_shares[kMaxDevices][4][2];
+struct PfSharesInit {
+  PfSharesInit() {
+    for (auto& d : g_pf_shares)
+      for (auto& t : d)
+        for (auto& h : t) h.store(-1);
+  }
+} g_pf_shares_init;
+
+int prefill_shares(pa_dtype dtype, int head_dim) {
+  if (dtype == PA_FP8_E4M3) return 0;  // no prefill kernel for E4M3 caches
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev >= kMaxDevices) return pa::prefill_resident_shares(dtype, head_dim);
+  std::atomic<int>& slot = g_pf_shares[dev][(int)dtype][head_dim == 128 ? 1 : 0];
+  int v = slot.load();
+  if (v < 0) {
+    v = pa::prefill_resident_shares(dtype, head_dim);
+    slot.store(v);
+  }
+  return v;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BalancedLayout {
@@ -143,23 +167,25 @@ BalancedLayout balanced_layout(int tw, int slot_rows, int head_dim, int num_seqs
 // request that fits one 16-row tile, whatever max_query_len says.
 int varlen_slot_rows(int group) { return (pa::kTileRows / group) * group; }
 
-// Varlen workspace: the balanced kernel's part, then the prefill split
-// partials [T, Hq, splits, D] and LSEs [T, Hq, splits] (splits from the block
-// table's width, which bounds every request's keys).
+// Varlen workspace: the balanced kernel's part, then the equal-share
+// prefill's partial rows [2 * shares, rows, D], their LSEs [2 * shares, rows]
+// and the per-token merge records [T, Hkv] (16 bytes each).
 struct VarlenLayout {
   BalancedLayout bal;
-  int pf_splits, pf_split_blocks;
-  size_t pf_o, pf_lse, total;
+  int pf_shares;
+  size_t pf_o, pf_lse, pf_rec, total;
 };
-VarlenLayout varlen_layout(int tw, int group, int head_dim, int num_seqs, int num_kv_heads,
-                           int num_tokens, int num_heads, int max_blocks_per_seq) {
+VarlenLayout varlen_layout(int tw, pa_dtype dtype, int group, int head_dim, int num_seqs,
+                           int num_kv_heads, int num_tokens, int num_heads) {
   VarlenLayout l;
   l.bal = balanced_layout(tw, varlen_slot_rows(group), head_dim, num_seqs, num_kv_heads);
-  pa::prefill_splits(max_blocks_per_seq, &l.pf_splits, &l.pf_split_blocks);
-  const size_t rows = (size_t)num_tokens * num_heads * (l.pf_splits > 1 ? l.pf_splits : 0);
+  (void)num_heads;
+  l.pf_shares = prefill_shares(dtype, head_dim);
+  const size_t rows = 2 * (size_t)l.pf_shares * (l.pf_shares > 0 ? pa::prefill_rows(dtype) : 0);
   l.pf_o = l.bal.total;
   l.pf_lse = l.pf_o + align256(rows * head_dim * sizeof(float));
-  l.total = l.pf_lse + align256(rows * sizeof(float));
+  l.pf_rec = l.pf_lse + align256(rows * sizeof(float));
+  l.total = l.pf_rec + align256(l.pf_shares > 0 ? (size_t)num_tokens * num_kv_heads * 16 : 0);
   return l;
 }
 
@@ -318,8 +344,9 @@ size_t pa_varlen_workspace_bytes(const pa_kv_cache* cache, int num_seqs, int num
   if (group > pa::kTileRows) return 0;
   const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
   if (tw <= 0) return 0;
-  return varlen_layout(tw, group, cache->head_dim, num_seqs, cache->num_kv_heads, num_tokens,
-                       num_heads, max_blocks_per_seq)
+  (void)max_blocks_per_seq;
+  return varlen_layout(tw, cache->dtype, group, cache->head_dim, num_seqs, cache->num_kv_heads,
+                       num_tokens, num_heads)
       .total;
 }
 
@@ -352,26 +379,26 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
   if (use_ws) {
     tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
     if (tw <= 0) return PA_ERR_LAUNCH;
-    vl = varlen_layout(tw, a.group, cache->head_dim, num_seqs, cache->num_kv_heads, num_tokens,
-                       num_heads, max_blocks_per_seq);
+    vl = varlen_layout(tw, cache->dtype, a.group, cache->head_dim, num_seqs,
+                       cache->num_kv_heads, num_tokens, num_heads);
     if (workspace_bytes < vl.total) return PA_ERR_WORKSPACE;
   }
   char* ws = static_cast<char*>(workspace);
   // prefill chunks (query rows x group > 16): the LDS-staged prefill kernel,
-  // long tiles cut into KV splits when the workspace holds their partials
+  // in equal shares over the resident workgroups when the workspace holds
+  // their partials, else one workgroup per (tile, request, KV head)
   if ((int64_t)max_query_len * a.group > 16) {
     if (cache->dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
     const int tt = pa::prefill_tile_tokens(cache->dtype, a.group);
     a.num_tiles = (max_query_len + tt - 1) / tt;
-    if (use_ws && vl.pf_splits > 1) {
-      a.pf_splits = vl.pf_splits;
-      a.pf_split_blocks = vl.pf_split_blocks;
+    if (use_ws && vl.pf_shares > 0) {
+      a.pf_shares = vl.pf_shares;
       a.pf_o = reinterpret_cast<float*>(ws + vl.pf_o);
       a.pf_lse = reinterpret_cast<float*>(ws + vl.pf_lse);
+      a.pf_rec = reinterpret_cast<int4*>(ws + vl.pf_rec);
     }
-    const int64_t pgrid =
-        (int64_t)a.num_tiles * num_seqs * cache->num_kv_heads * a.pf_splits;
-    if (pgrid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    const int64_t pgrid = (int64_t)a.num_tiles * num_seqs * cache->num_kv_heads;
+    if (a.pf_shares == 0 && pgrid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     pa_status ps = launched(pa::launch_prefill(a, cache->dtype, cache->head_dim, pgrid, st));
     if (ps != PA_OK) return ps;
     ps = launched(pa::launch_prefill_merge(a, cache->dtype, cache->head_dim, st));

@@ -32,13 +32,14 @@ struct AttnArgs {
   float scale_log2;          // scale * log2(e) (times the K scale of an E4M3 cache)
   float out_scale;           // output factor: the V scale of an E4M3 cache, else 1
   int causal;
-  // Prefill KV splits: a prefill tile whose keys span more than
-  // pf_split_blocks blocks is processed as several splits that write
-  // partials here (else every tile writes its output directly).
-  float* pf_o;               // [T, Hq, pf_splits, D] normalised partial outputs, or nullptr
-  float* pf_lse;             // [T, Hq, pf_splits] partial LSEs (log2 domain)
-  int pf_splits;             // splits per tile (1: no splits)
-  int pf_split_blocks;       // KV blocks per split
+  // Prefill in equal shares (pf_shares > 0): pf_shares workgroups each take
+  // an equal contiguous share of the batch's (request, KV head, tile, KV
+  // block) items; pieces that cut a tile write partials here. With
+  // pf_shares == 0, one workgroup per (tile, request, KV head), no partials.
+  float* pf_o;               // [2 * pf_shares, prefill_rows, D] normalised partial rows
+  float* pf_lse;             // [2 * pf_shares, prefill_rows] partial LSEs (log2 domain)
+  int4* pf_rec;              // [T, Hkv] per token: (first slot, pieces, row in slot, 0)
+  int pf_shares;
 };
 
 struct MergeArgs {
@@ -116,14 +117,19 @@ hipError_t launch_attention(const AttnArgs& args, pa_dtype dtype, int head_dim, 
 hipError_t launch_lse_merge(const MergeArgs& args, pa_dtype out_dtype, hipStream_t stream);
 // Query tokens one prefill workgroup covers for GQA group size `group`.
 int prefill_tile_tokens(pa_dtype dtype, int group);
-// Prefill KV splits for keys up to max_blocks blocks: *splits splits of
-// *split_blocks blocks (*splits == 1: none).
-void prefill_splits(int max_blocks, int* splits, int* split_blocks);
-// Merges the split partials of prefill tiles into `a.out`.
-hipError_t launch_prefill_merge(const AttnArgs& a, pa_dtype dtype, int head_dim,
-                                hipStream_t stream);
+// Query rows of one prefill tile (partial rows per slot).
+int prefill_rows(pa_dtype dtype);
+// Resident workgroups of the equal-share prefill kernel on the current
+// device (0 on error).
+int prefill_resident_shares(pa_dtype dtype, int head_dim);
+// Prefill rows of a varlen step: the equal-share kernel when a.pf_shares > 0
+// (grid ignored), else `grid` workgroups, one per (tile, request, KV head).
 hipError_t launch_prefill(const AttnArgs& args, pa_dtype dtype, int head_dim, int64_t grid,
                           hipStream_t stream);
+// Merges the cut tiles of the equal-share prefill into `a.out` (no-op when
+// a.pf_shares == 0).
+hipError_t launch_prefill_merge(const AttnArgs& a, pa_dtype dtype, int head_dim,
+                                hipStream_t stream);
 // Resident waves of the balanced decode kernel on the current device for
 // this head count (0 on error).
 int balanced_total_waves(pa_dtype dtype, int head_dim, int num_kv_heads);

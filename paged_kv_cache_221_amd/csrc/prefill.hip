@@ -10,6 +10,17 @@
 // blocks, and each wave reads the block's MFMA operands from LDS once and
 // applies them to all of its RT row tiles. Scores and probabilities stay in
 // registers (the FlashAttention principle [P3 §3.4]).
+//
+// A workgroup's time is its tile's key count, which in a causal chunk grows
+// with the tile's position and with the request's cached context: one
+// workgroup per (tile, request, KV head) leaves most CUs idle while the last
+// tiles of the longest request finish (the mixed step's 4k-context chunk
+// holds half the work in a quarter of the workgroups). With a workspace, the
+// batch's (request, KV head, tile, KV block) items are instead cut into one
+// equal contiguous share per resident workgroup, like the balanced decode
+// kernel; a tile cut between shares is written as partials (normalised
+// output and log-sum-exp per piece) and renormalised by a small merge kernel
+// [P1 §07 LSE merge].
 #include "attn_tile.h"
 #include "pa_launch.h"
 
@@ -22,16 +33,11 @@
 #ifndef PA_PREFILL_OCC
 #define PA_PREFILL_OCC 2
 #endif
-// KV blocks per split of a long prefill tile, and the most splits per tile
-// (longer contexts get longer splits). Splits only pay when the prefill
-// tiles cannot fill the GPU: on the mixed step (4 chunks of 512 tokens on
-// contexts up to 4k, 512 workgroups) 96-block splits made the prefill slower
-// (254 -> 280 us), because its workgroups already keep every CU busy.
-#ifndef PA_PREFILL_SPLIT_BLOCKS
-#define PA_PREFILL_SPLIT_BLOCKS 512
-#endif
-#ifndef PA_PREFILL_MAX_SPLITS
-#define PA_PREFILL_MAX_SPLITS 8
+// Fixed cost of a tile in the equal-share prefill, in KV blocks: a piece
+// pays its query loads, pipeline fill and stores, so shares of many short
+// tiles get fewer blocks.
+#ifndef PA_PREFILL_TILE_COST
+#define PA_PREFILL_TILE_COST 2
 #endif
 
 namespace pa {
@@ -60,47 +66,61 @@ struct Stage {
   };
 };
 
-template <class E, int D, int RT, int RING>
-__global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kernel(const AttnArgs a) {
-  using O = Ops<E, D>;
-  using S = typename O::storage;
-  using St = Stage<E, D>;
-  __shared__ __attribute__((aligned(16))) char s_k[2][kBlockTokens * St::kLdsRow];
-  __shared__ __attribute__((aligned(16))) char s_v[2][kBlockTokens * St::kLdsRow];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  // tiles in descending order: the tiles that see the most keys start first
-  int u = blockIdx.x;
-  const int kvh = u % a.num_kv_heads;
-  u /= a.num_kv_heads;
-  const int split = u % a.pf_splits;
-  u /= a.pf_splits;
-  const int r = u % a.num_seqs;
-  const int tile = a.num_tiles - 1 - u / a.num_seqs;
-
+// Query rows and keys of one prefill request (cu_seqlens and seq_lens
+// clamped to the batch and the block table like the other kernels).
+struct PfRequest {
+  int q_lo, n, seq_len, ctx;
+};
+__device__ inline PfRequest pf_request(const AttnArgs& a, int r) {
   int lo = a.cu_seqlens[r], hi = a.cu_seqlens[r + 1];
   lo = min(max(lo, 0), a.num_tokens);
   hi = min(max(hi, lo), a.num_tokens);
-  const int q_lo = lo, n = hi - lo;
+  PfRequest q;
+  q.q_lo = lo;
+  q.n = hi - lo;
+  q.seq_len = min(max(a.seq_lens[r], 0), a.max_blocks * kBlockTokens);
+  q.ctx = max(q.seq_len - q.n, 0);
+  return q;
+}
+// A request is a prefill chunk when its query rows fill more than one tile.
+__device__ inline bool pf_is_prefill(const PfRequest& q, int g) { return q.n * g > kTileRows; }
+__device__ inline int pf_tiles(const PfRequest& q, int tile_tokens) {
+  return (q.n + tile_tokens - 1) / tile_tokens;
+}
+// KV blocks tile `tile` reads: keys up to its last row's causal limit.
+__device__ inline int pf_tile_blocks(const AttnArgs& a, const PfRequest& q, int tile,
+                                     int tile_tokens) {
+  const int tile_end = min((tile + 1) * tile_tokens, q.n);
+  const int kmax = a.causal ? min(q.ctx + tile_end, q.seq_len) : q.seq_len;
+  return (kmax + kBlockTokens - 1) / kBlockTokens;
+}
+
+// Double-buffered LDS copies of one KV block's head slice.
+template <class E, int D>
+struct PfLds {
+  char k[2][kBlockTokens * Stage<E, D>::kLdsRow];
+  char v[2][kBlockTokens * Stage<E, D>::kLdsRow];
+};
+
+// One piece: KV blocks [b0, b1) of tile `tile` of request r (rq) for KV
+// head kvh, against all the tile's query rows (each wave RT row tiles). With
+// slot < 0 the piece is the whole tile and its rows go to the output; else
+// its normalised partial rows and log2-domain LSEs go to partial slot `slot`
+// (rows in tile order: (wave * RT + rt) * 16 + row). Called by every thread
+// of the workgroup; the caller separates consecutive pieces by a barrier.
+template <class E, int D, int RT, int RING>
+__device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfRequest& rq, int r,
+                                int kvh, int tile, int b0, int b1, int64_t slot) {
+  using O = Ops<E, D>;
+  using S = typename O::storage;
+  using St = Stage<E, D>;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = a.group;
-  if (n * g <= 16) return;  // a single-tile request: handled by the decode kernel
-  const int seq_len = min(max(a.seq_lens[r], 0), a.max_blocks * kBlockTokens);
-  const int ctx = max(seq_len - n, 0);
-  const int tpw = 16 / g;                               // tokens per row tile
-  const int tile_tokens = kPrefillWaves * RT * tpw;
-  const int tok_base = tile * tile_tokens;
-  if (tok_base >= n) return;
-  const int tile_end = min(tok_base + tile_tokens, n);
-  const int kmax = a.causal ? min(ctx + tile_end, seq_len) : seq_len;
-  const int nblk = (kmax + kBlockTokens - 1) / kBlockTokens;
-  if (nblk <= 0) return;
-  // this workgroup's blocks [b0, b1) of the tile's nblk
-  const int nsplit = a.pf_splits > 1 ? (nblk + a.pf_split_blocks - 1) / a.pf_split_blocks : 1;
-  if (split >= nsplit) return;
-  const int b0 = nsplit > 1 ? split * a.pf_split_blocks : 0;
-  const int b1 = nsplit > 1 ? min(b0 + a.pf_split_blocks, nblk) : nblk;
+  const int tpw = kTileRows / g;                        // tokens per row tile
+  const int tok_base = tile * (kPrefillWaves * RT * tpw);
+  const int n = rq.n, seq_len = rq.seq_len, ctx = rq.ctx, q_lo = rq.q_lo;
 
   // this wave's row tiles
   const int row = lane & 15, grp = lane >> 4;
@@ -151,11 +171,16 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
       const int c = tid + p * kPrefillThreads;
       if (c < St::kChunks) {
         const int off = (c / St::kChunksPerRow) * St::kLdsRow + (c % St::kChunksPerRow) * 16;
-        *reinterpret_cast<u32x4*>(&s_k[buf][off]) = rg.k[p];
-        *reinterpret_cast<u32x4*>(&s_v[buf][off]) = rg.v[p];
+        *reinterpret_cast<u32x4*>(&lds.k[buf][off]) = rg.k[p];
+        *reinterpret_cast<u32x4*>(&lds.v[buf][off]) = rg.v[p];
       }
     }
   };
+
+  // keys at or past b1 * 16 belong to the next piece
+  int kend[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) kend[rt] = min(key_end[rt], b1 * kBlockTokens);
 
   typename St::Regs ring[RING];
 #pragma unroll
@@ -170,18 +195,16 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
       __builtin_amdgcn_sched_barrier(0);
       issue(ring[j], i + RING);
       __builtin_amdgcn_sched_barrier(0);
-      // Unconditional, like the loads: a padding block past b1 was read as
-      // zeros and is fully masked (b1 < nblk only before the last split,
-      // whose keys come after), so it adds nothing, and the accumulators stay
-      // in one set of registers.
+      // Unconditional, like the loads: a padding block at or past b1 was
+      // read as zeros and its keys are past every row's limit (kend), so it
+      // adds nothing, and the accumulators stay in one set of registers.
       typename O::KV kv;
-      O::load_lds(kv, s_k[buf], s_v[buf], St::kLdsRow, lane);
-      consume_block_tiles<E, D, RT>(st, kv, q, i * kBlockTokens, key_end, a.scale_log2, lane);
+      O::load_lds(kv, lds.k[buf], lds.v[buf], St::kLdsRow, lane);
+      consume_block_tiles<E, D, RT>(st, kv, q, i * kBlockTokens, kend, a.scale_log2, lane);
     }
   }
 
-  // epilogue: normalise and store every valid row (a split's partial when
-  // the tile has several splits)
+  // epilogue: normalise and store every valid row (partials when cut)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     st[rt].l = sum_xor16(st[rt].l);
@@ -190,8 +213,8 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
     const int tok = tok0 + row / g, hh = row - (row / g) * g;
     if (row < tpw * g && tok < n) {
       const float inv = st[rt].l > 0.f ? 1.f / st[rt].l : 0.f;
-      const int64_t orow = (int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh;
-      if (nsplit == 1) {
+      if (slot < 0) {
+        const int64_t orow = (int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh;
         S* dst = static_cast<S*>(a.out) + orow * D + (D / 4) * grp;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -201,7 +224,8 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
           store_chunk<E, D>(dst + (D / 16) * i, v);
         }
       } else {
-        const int64_t prow = orow * a.pf_splits + split;
+        const int64_t prow =
+            slot * (kPrefillWaves * RT * kTileRows) + (wave * RT + rt) * kTileRows + row;
         float* dst = a.pf_o + prow * D + (D / 4) * grp;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -216,74 +240,248 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
   }
 }
 
-// Merges the splits of long prefill tiles [P1 §07 LSE merge]: one wave per
-// (query token, head). Tokens of single-tile requests and of tiles that had
-// one split were written directly and are skipped. The tile's split count is
-// recomputed exactly as prefill_kernel derives it; it never exceeds
-// pf_splits because keys are clipped to the block table's width, from which
-// pf_splits is sized.
+// One workgroup per (tile, request, KV head), tiles in descending order (the
+// tiles that see the most keys start first); every tile written whole.
+template <class E, int D, int RT, int RING>
+__global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) PfLds<E, D> lds;
+  int u = blockIdx.x;
+  const int kvh = u % a.num_kv_heads;
+  u /= a.num_kv_heads;
+  const int r = u % a.num_seqs;
+  const int tile = a.num_tiles - 1 - u / a.num_seqs;
+  const PfRequest rq = pf_request(a, r);
+  if (!pf_is_prefill(rq, a.group)) return;  // a single-tile request: the decode kernel's
+  const int tile_tokens = kPrefillWaves * RT * (kTileRows / a.group);
+  if (tile * tile_tokens >= rq.n) return;
+  const int nblk = pf_tile_blocks(a, rq, tile, tile_tokens);
+  if (nblk <= 0) return;
+  pf_piece<E, D, RT, RING>(a, lds, rq, r, kvh, tile, 0, nblk, -1);
+}
+
+// Exclusive prefix sum over the workgroup (int64); *total gets the sum.
+__device__ inline int64_t pf_exclusive_sum(int64_t v, int64_t* s_tmp, int64_t* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int64_t x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int64_t y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) s_tmp[wave] = x;
+  __syncthreads();
+  int64_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kPrefillWaves; ++w) {
+    const int64_t t = s_tmp[w];
+    off += w < wave ? t : 0;
+    tot += t;
+  }
+  *total = tot;
+  return off + x - v;
+}
+
+// Share items of a tile: its KV blocks plus the fixed tile cost (0 for a
+// tile with no keys, which has nothing to do).
+__device__ inline int pf_tile_items(int nblk) { return nblk > 0 ? nblk + PA_PREFILL_TILE_COST : 0; }
+
+// Share items summed over all tiles of a prefill request (one KV head).
+__device__ inline int64_t pf_request_items(const AttnArgs& a, const PfRequest& rq,
+                                           int tile_tokens) {
+  const int tiles = pf_tiles(rq, tile_tokens);
+  int64_t sum = 0;
+  for (int t = 0; t < tiles; ++t) sum += pf_tile_items(pf_tile_blocks(a, rq, t, tile_tokens));
+  return sum;
+}
+
+// Writes the merge record of every query token of a tile for one KV head:
+// first partial slot, piece count (0: the tile was written whole) and the
+// token's first row in the tile's partial slot.
+__device__ inline void pf_write_records(const AttnArgs& a, const PfRequest& rq, int kvh,
+                                        int tile, int tile_tokens, int s0, int cnt) {
+  const int g = a.group, tpw = kTileRows / g;
+  const int t0 = tile * tile_tokens;
+  const int nt = min(tile_tokens, rq.n - t0);
+  for (int i = threadIdx.x; i < nt; i += kPrefillThreads)
+    a.pf_rec[(int64_t)(rq.q_lo + t0 + i) * a.num_kv_heads + kvh] =
+        int4{s0, cnt, (i / tpw) * kTileRows + (i % tpw) * g, 0};
+}
+
+// Equal shares: the W items -- (request, KV head, tile, KV block) in that
+// order, prefill requests only, each tile followed by PA_PREFILL_TILE_COST
+// items that stand for its fixed cost -- are cut into T = min(pf_shares, W)
+// contiguous shares with floor-spaced bounds, one per workgroup (share index
+// XCD-major, so neighbouring shares, which mostly read the same request's
+// blocks, share an L2). A share walks its pieces; a piece that is a whole
+// tile writes the output rows, a cut one its partial slot: 2j for the
+// share's first piece, 2j + 1 for its last (only these two can be cut).
+// Every piece of a tile writes the records of the tile's tokens (first slot,
+// piece count -- 0: written whole -- and row), for the merge; workgroup 0
+// writes empty records for the batch's other tokens.
+template <class E, int D, int RT, int RING>
+__global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_shares_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) PfLds<E, D> lds;
+  __shared__ int64_t s_pre[kMaxBalancedSeqs + 1];
+  __shared__ int64_t s_tmp[kPrefillWaves];
+  const int tid = threadIdx.x;
+  const int B = a.num_seqs, hkv = a.num_kv_heads, g = a.group;
+  const int tile_tokens = kPrefillWaves * RT * (kTileRows / g);
+
+  // 1. items before each request, in LDS
+  const int per = (B + kPrefillThreads - 1) / kPrefillThreads;
+  const int c0 = min(tid * per, B), c1 = min(c0 + per, B);
+  int64_t chunk = 0;
+  for (int i = c0; i < c1; ++i) {
+    const PfRequest rq = pf_request(a, i);
+    const int64_t items = pf_is_prefill(rq, g) ? hkv * pf_request_items(a, rq, tile_tokens) : 0;
+    s_pre[i + 1] = items;
+    chunk += items;
+    if (blockIdx.x == 0) {
+      // tokens no piece covers get an empty record: single-tile requests'
+      // tokens and those of tiles without keys
+      const bool pre = pf_is_prefill(rq, g);
+      for (int t = 0; t < (pre ? pf_tiles(rq, tile_tokens) : 1); ++t) {
+        if (pre && pf_tile_blocks(a, rq, t, tile_tokens) > 0) continue;
+        const int lo_t = pre ? t * tile_tokens : 0;
+        const int hi_t = pre ? min(lo_t + tile_tokens, rq.n) : rq.n;
+        for (int tok = lo_t; tok < hi_t; ++tok)
+          for (int k = 0; k < hkv; ++k)
+            a.pf_rec[(int64_t)(rq.q_lo + tok) * hkv + k] = int4{0, 0, 0, 0};
+      }
+    }
+  }
+  int64_t W = 0;
+  int64_t run = pf_exclusive_sum(chunk, s_tmp, &W);
+  for (int i = c0; i < c1; ++i) {
+    run += s_pre[i + 1];
+    s_pre[i + 1] = run;
+  }
+  if (tid == 0) s_pre[0] = 0;
+  __syncthreads();
+
+  // 2. this workgroup's share
+  const int64_t T = min((int64_t)a.pf_shares, W);
+  const int nx = (int)gridDim.x;
+  const int64_t j = (nx % 8 == 0) ? (int64_t)(blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8
+                                  : (int64_t)blockIdx.x;
+  if (j >= T) return;
+  auto begin_of = [&](int64_t t) { return t * W / T; };
+  auto share_of = [&](int64_t x) { return ((x + 1) * T - 1) / W; };  // share holding item x
+  const int64_t lo = begin_of(j), hi = begin_of(j + 1);
+  int r_lo = 0, r_hi = B - 1;
+  while (r_lo < r_hi) {
+    const int mid = (r_lo + r_hi + 1) >> 1;
+    if (s_pre[mid] <= lo) r_lo = mid; else r_hi = mid - 1;
+  }
+  int r = r_lo;
+  int64_t x = lo;
+  bool first = true;
+  while (x < hi) {
+    while (r < B - 1 && s_pre[r + 1] <= x) ++r;
+    const PfRequest rq = pf_request(a, r);
+    const int64_t per_head = (s_pre[r + 1] - s_pre[r]) / hkv;
+    const int64_t off = x - s_pre[r];
+    const int kvh = (int)(off / per_head);
+    int64_t rem = off - (int64_t)kvh * per_head;
+    int tile = 0, nblk = pf_tile_blocks(a, rq, 0, tile_tokens), nit = pf_tile_items(nblk);
+    while (rem >= nit) {
+      rem -= nit;
+      ++tile;
+      nblk = pf_tile_blocks(a, rq, tile, tile_tokens);
+      nit = pf_tile_items(nblk);
+    }
+    const int b0 = (int)rem;
+    const int len = (int)min((int64_t)(nit - b0), hi - x);
+    // the piece's KV blocks: items past nblk are the tile's fixed cost
+    const int b1 = min(b0 + len, nblk);
+    if (b0 < b1) {
+      const bool whole = b0 == 0 && b1 == nblk;
+      const int64_t slot = whole ? -1 : 2 * j + (x == lo ? 0 : 1);
+      if (!first) __syncthreads();  // the previous piece's LDS reads are done
+      first = false;
+      pf_piece<E, D, RT, RING>(a, lds, rq, r, kvh, tile, b0, b1, slot);
+      int s0 = 0, cnt = 0;
+      if (!whole) {
+        // shares holding the tile's first and last KV block
+        const int64_t t_begin = x - b0, t_last = t_begin + nblk - 1;
+        const int64_t j0 = share_of(t_begin), j1 = share_of(t_last);
+        s0 = (int)(2 * j0 + (t_begin == begin_of(j0) ? 0 : 1));
+        cnt = (int)(j1 - j0 + 1);
+      }
+      pf_write_records(a, rq, kvh, tile, tile_tokens, s0, cnt);
+    }
+    x += len;
+  }
+}
+
+// Renormalises the cut tiles of the equal-share prefill [P1 §07 LSE merge]:
+// one wave per (query token, KV head), its g heads side by side (lph lanes
+// per head, D / lph >= 4 dims per lane). The token's record names its tile's
+// first partial slot s0 and piece count c (0: nothing to merge); piece p > 0
+// sits at slot 2 (s0 / 2 + p), the first piece of each later share. Pieces
+// are folded in with a running maximum, so their loads do not wait for each
+// other. A record naming slots past the workspace is ignored.
 template <class E>
-__global__ __launch_bounds__(4 * kWave) void prefill_merge_kernel(const AttnArgs a,
-                                                                  int tile_tokens, int D) {
+__global__ __launch_bounds__(4 * kWave) void prefill_share_merge_kernel(const AttnArgs a,
+                                                                        int pf_rows, int D) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  if (unit >= (int64_t)a.num_tokens * a.num_heads) return;
-  const int token = (int)(unit / a.num_heads);
-  // the request holding this token: the largest r with cu[r] <= token
-  int lo = 0, hi = a.num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.cu_seqlens[mid] <= token) lo = mid; else hi = mid - 1;
+  if (unit >= (int64_t)a.num_tokens * a.num_kv_heads) return;
+  const int4 rec = a.pf_rec[unit];  // unit = token * Hkv + kvh
+  const int s0 = rec.x, cnt = rec.y;
+  const int64_t slots = 2 * (int64_t)a.pf_shares;
+  if (cnt <= 0 || s0 < 0 || s0 >= slots || 2 * ((int64_t)(s0 >> 1) + cnt - 1) >= slots) return;
+  const int g = a.group;
+  int gp = 1;
+  while (gp < g) gp <<= 1;
+  const int lph = min(kWave / gp, D / 4);  // lanes per head
+  const int hh = lane / lph;
+  if (hh >= g) return;
+  const int dpl = D / lph;                 // dims per lane: 4 .. 32 for g <= 16
+  const int d0 = (lane % lph) * dpl;
+  const int64_t prow = rec.z + hh;
+  constexpr int kMaxDpl = 32;
+  float acc[kMaxDpl];
+#pragma unroll
+  for (int i = 0; i < kMaxDpl; ++i) acc[i] = 0.f;
+  float m = neg_inf(), l = 0.f;
+  for (int p = 0; p < cnt; ++p) {
+    const int64_t sr = (p == 0 ? s0 : 2 * ((int64_t)(s0 >> 1) + p)) * pf_rows + prow;
+    const float lse = a.pf_lse[sr];
+    const float* o = a.pf_o + sr * D + d0;
+    float v[kMaxDpl];
+#pragma unroll
+    for (int i = 0; i < kMaxDpl; i += 4) {
+      if (i < dpl) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(o + i);
+        v[i] = x[0];
+        v[i + 1] = x[1];
+        v[i + 2] = x[2];
+        v[i + 3] = x[3];
+      }
+    }
+    const float mn = fmaxf(m, lse);
+    if (mn == neg_inf()) continue;     // no piece with keys yet
+    const float alpha = fast_exp2(m - mn), w = fast_exp2(lse - mn);
+#pragma unroll
+    for (int i = 0; i < kMaxDpl; ++i)
+      if (i < dpl) acc[i] = acc[i] * alpha + w * v[i];
+    l = l * alpha + w;
+    m = mn;
   }
-  const int r = lo;
-  int q_lo = a.cu_seqlens[r], q_hi = a.cu_seqlens[r + 1];
-  q_lo = min(max(q_lo, 0), a.num_tokens);
-  q_hi = min(max(q_hi, q_lo), a.num_tokens);
-  if (token < q_lo || token >= q_hi) return;
-  const int n = q_hi - q_lo, g = a.group;
-  if (n * g <= 16) return;
-  const int seq_len = min(max(a.seq_lens[r], 0), a.max_blocks * kBlockTokens);
-  const int ctx = max(seq_len - n, 0);
-  const int tile_end = min(((token - q_lo) / tile_tokens + 1) * tile_tokens, n);
-  const int kmax = a.causal ? min(ctx + tile_end, seq_len) : seq_len;
-  const int nblk = (kmax + kBlockTokens - 1) / kBlockTokens;
-  const int nsplit = (nblk + a.pf_split_blocks - 1) / a.pf_split_blocks;
-  if (nsplit <= 1) return;
-  const int64_t prow = unit * a.pf_splits;  // unit = token * Hq + head
-  const int d0 = lane, d1 = lane + kWave;
-  // outputs of every split, loaded together with the LSEs
-  float x0[PA_PREFILL_MAX_SPLITS], x1[PA_PREFILL_MAX_SPLITS];
-#pragma unroll
-  for (int j = 0; j < PA_PREFILL_MAX_SPLITS; ++j) {
-    const bool ok = j < nsplit;
-    x0[j] = ok && d0 < D ? a.pf_o[(prow + j) * D + d0] : 0.f;
-    x1[j] = ok && d1 < D ? a.pf_o[(prow + j) * D + d1] : 0.f;
-  }
-  const float lse = lane < nsplit ? a.pf_lse[prow + lane] : neg_inf();
-  float mx = lse;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, xor_shuffle(mx, m));
-  const float mu = mx == neg_inf() ? 0.f : mx;
-  const float w = lane < nsplit ? fast_exp2(lse - mu) : 0.f;
-  float wsum = w;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) wsum += xor_shuffle(wsum, m);
-  float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-  for (int j = 0; j < PA_PREFILL_MAX_SPLITS; ++j) {
-    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
-    acc0 += wj * x0[j];  // zero past nsplit (loaded as 0, weight 0)
-    acc1 += wj * x1[j];
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   using S = typename E::storage;
-  S* out = static_cast<S*>(a.out) + unit * D;
-  if constexpr (sizeof(S) == 2) {
-    if (d0 < D) out[d0] = E::from_float(acc0 * inv);
-    if (d1 < D) out[d1] = E::from_float(acc1 * inv);
-  } else {
-    if (d0 < D) out[d0] = acc0 * inv;
-    if (d1 < D) out[d1] = acc1 * inv;
+  const int token = (int)(unit / a.num_kv_heads), kvh = (int)(unit - (int64_t)token * a.num_kv_heads);
+  S* out = static_cast<S*>(a.out) + ((int64_t)token * a.num_heads + kvh * g + hh) * D + d0;
+#pragma unroll
+  for (int i = 0; i < kMaxDpl; ++i) {
+    if (i < dpl) {
+      if constexpr (sizeof(S) == 2) {
+        out[i] = E::from_float(acc[i] * inv);
+      } else {
+        out[i] = acc[i] * inv;
+      }
+    }
   }
 }
 
@@ -304,44 +502,79 @@ hipError_t launch_pf(const AttnArgs& a, int64_t grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-void prefill_splits(int max_blocks, int* splits, int* split_blocks) {
-  int sp = (max_blocks + PA_PREFILL_SPLIT_BLOCKS - 1) / PA_PREFILL_SPLIT_BLOCKS;
-  sp = min(max(sp, 1), PA_PREFILL_MAX_SPLITS);
-  *splits = sp;
-  *split_blocks = max((max_blocks + sp - 1) / sp, 1);
-}
-
-hipError_t launch_prefill_merge(const AttnArgs& a, pa_dtype dtype, int head_dim,
-                                hipStream_t stream) {
-  const int64_t units = (int64_t)a.num_tokens * a.num_heads;
-  if (units <= 0 || a.pf_splits <= 1) return hipSuccess;
-  const int tt = prefill_tile_tokens(dtype, a.group);
-  const dim3 grid((unsigned)((units + 3) / 4)), block(4 * kWave);
-  switch (dtype) {
-    case PA_BF16: prefill_merge_kernel<Bf16><<<grid, block, 0, stream>>>(a, tt, head_dim); break;
-    case PA_F16: prefill_merge_kernel<F16><<<grid, block, 0, stream>>>(a, tt, head_dim); break;
-    case PA_F32: prefill_merge_kernel<F32><<<grid, block, 0, stream>>>(a, tt, head_dim); break;
-    default: return hipErrorInvalidValue;
-  }
+template <class E, int D>
+hipError_t launch_pf_shares(const AttnArgs& a, hipStream_t stream) {
+  prefill_shares_kernel<E, D, prefill_rt<E>(), prefill_ring<E>()>
+      <<<dim3((unsigned)a.pf_shares), dim3(kPrefillThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
+template <class E, int D>
+int resident_pf_shares() {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, prefill_shares_kernel<E, D, prefill_rt<E>(), prefill_ring<E>()>,
+          kPrefillThreads, 0) != hipSuccess)
+    return 0;
+  return per_cu * cus;
+}
+
+}  // namespace
+
 int prefill_tile_tokens(pa_dtype dtype, int group) {
   const int rt = dtype == PA_F32 ? prefill_rt<F32>() : prefill_rt<Bf16>();
-  return kPrefillWaves * rt * (16 / group);
+  return kPrefillWaves * rt * (kTileRows / group);
+}
+
+int prefill_rows(pa_dtype dtype) {
+  const int rt = dtype == PA_F32 ? prefill_rt<F32>() : prefill_rt<Bf16>();
+  return kPrefillWaves * rt * kTileRows;
+}
+
+int prefill_resident_shares(pa_dtype dtype, int head_dim) {
+  switch (dtype) {
+    case PA_BF16: return head_dim == 128 ? resident_pf_shares<Bf16, 128>() : resident_pf_shares<Bf16, 64>();
+    case PA_F16: return head_dim == 128 ? resident_pf_shares<F16, 128>() : resident_pf_shares<F16, 64>();
+    case PA_F32: return head_dim == 128 ? resident_pf_shares<F32, 128>() : resident_pf_shares<F32, 64>();
+    default: return 0;
+  }
 }
 
 hipError_t launch_prefill(const AttnArgs& a, pa_dtype dtype, int head_dim, int64_t grid,
                           hipStream_t stream) {
+  if (a.pf_shares > 0) {
+    switch (dtype) {
+      case PA_BF16: return head_dim == 128 ? launch_pf_shares<Bf16, 128>(a, stream) : launch_pf_shares<Bf16, 64>(a, stream);
+      case PA_F16: return head_dim == 128 ? launch_pf_shares<F16, 128>(a, stream) : launch_pf_shares<F16, 64>(a, stream);
+      case PA_F32: return head_dim == 128 ? launch_pf_shares<F32, 128>(a, stream) : launch_pf_shares<F32, 64>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (grid <= 0) return hipSuccess;
   switch (dtype) {
     case PA_BF16: return head_dim == 128 ? launch_pf<Bf16, 128>(a, grid, stream) : launch_pf<Bf16, 64>(a, grid, stream);
     case PA_F16: return head_dim == 128 ? launch_pf<F16, 128>(a, grid, stream) : launch_pf<F16, 64>(a, grid, stream);
     case PA_F32: return head_dim == 128 ? launch_pf<F32, 128>(a, grid, stream) : launch_pf<F32, 64>(a, grid, stream);
+    default: return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_merge(const AttnArgs& a, pa_dtype dtype, int head_dim,
+                                hipStream_t stream) {
+  const int64_t units = (int64_t)a.num_tokens * a.num_kv_heads;
+  if (units <= 0 || a.pf_shares <= 0) return hipSuccess;
+  const int rows = prefill_rows(dtype);
+  const dim3 grid((unsigned)((units + 3) / 4)), block(4 * kWave);
+  switch (dtype) {
+    case PA_BF16: prefill_share_merge_kernel<Bf16><<<grid, block, 0, stream>>>(a, rows, head_dim); break;
+    case PA_F16: prefill_share_merge_kernel<F16><<<grid, block, 0, stream>>>(a, rows, head_dim); break;
+    case PA_F32: prefill_share_merge_kernel<F32><<<grid, block, 0, stream>>>(a, rows, head_dim); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace pa

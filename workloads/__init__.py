@@ -12,6 +12,7 @@ from .configs import (  # noqa: F401
     long_context_splitk,
     llama2_7b_mha_decode,
     mixed_step,
+    mixed_step_prefill_only,
     small_decode,
     small_varlen,
 )

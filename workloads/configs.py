@@ -75,6 +75,16 @@ def mixed_step(seed: int = 5, shuffled: bool = False) -> StepLayout:
     return permute_requests(layout, seed + 2000) if shuffled else layout
 
 
+def mixed_step_prefill_only(seed: int = 5) -> StepLayout:
+    """The mixed step's 4 prefill chunks alone (512 new tokens on contexts
+    0/1k/2k/4k), for the compute rate of the prefill rows."""
+    prefill_ctx = [0, 1024, 2048, 4096]
+    return build_layout("mixed-step-prefill-chunks-bf16", "bf16", [c + 512 for c in prefill_ctx],
+                        [512] * 4, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                        seed=seed, pool_factor=1.2, max_blocks_per_seq=8192 // 16,
+                        value_std=0.5)
+
+
 BENCH_CONFIGS = {
     "tiny-decode-fp32": tiny_decode_fp32,
     "llama3-8b-decode-bf16": llama3_8b_decode,
