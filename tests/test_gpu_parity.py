@@ -330,8 +330,9 @@ def test_binding_rejects_bad_arguments(gpu_lib):
                                   ("f32", 128, 8, 2)], ids=lambda c: "-".join(map(str, c)))
 def test_varlen_long_prefill_tiles(gpu_lib, case, path):
     """Prefill chunks spanning several workgroup tiles with ragged ends, next to
-    decode rows; the chunk on a 9,000-token context spans ~565 KV blocks, so
-    with a workspace its tiles run as two KV splits merged afterwards."""
+    decode rows; the chunk on a 9,000-token context spans ~565 KV blocks per
+    tile, so with a workspace its tiles are cut between several equal shares
+    and merged afterwards."""
     dtype, d, hq, hkv = case
     lay = small_varlen(400 + hq, dtype=dtype, num_heads=hq, num_kv_heads=hkv, head_dim=d,
                        prefill=((300, 100), (129, 0), (65, 700), (40, 9000)),

@@ -1,0 +1,93 @@
+"""GPU parity of the prefill rows of pa_varlen in equal shares (with a
+workspace) and per tile (without), against the oracle.
+
+The shares cut tiles at arbitrary KV blocks, so these cases aim at the
+merge: GQA groups whose heads do not fill a power of two (3) or fill a whole
+tile row (16), a tile cut into ~190 one-block pieces (one KV head, few items:
+one item per share), and a workspace reused across batches in which the same
+token positions change from prefill to decode rows, whose stale merge
+records must not touch the new batch.
+"""
+
+import pytest
+import torch
+
+import paged_kv_cache_221_amd as pa
+from workloads import build_layout, small_varlen
+from workloads.tensors import materialize
+
+from _parity import TOL, gpu_rows, gpu_write, max_err, prepare, varlen_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(st, lay, workspace, causal=True):
+    return pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                        st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
+                        causal=causal, workspace=workspace)
+
+
+@pytest.mark.parametrize("path", ["shares", "per-tile"])
+@pytest.mark.parametrize("case", [("bf16", 128, 6, 2, True), ("bf16", 64, 16, 1, True),
+                                  ("f16", 128, 12, 4, False), ("f32", 64, 16, 1, True)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_prefill_group_sizes(gpu_lib, case, path):
+    dtype, d, hq, hkv, causal = case
+    lay = small_varlen(500 + hq + d, dtype=dtype, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       prefill=((60, 0), (33, 100), (200, 40), (7, 300)),
+                       decode_lens=(1, 50, 17))
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    out = _run(st, lay, "auto" if path == "shares" else None, causal)
+    torch.cuda.synchronize()
+    want, _ = varlen_oracle(st, snap, req, causal=causal)
+    err = max_err(gpu_rows(out, dtype), want)
+    print(f"{lay.name} {path} causal={causal}: max|err| = {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+def test_prefill_tile_cut_into_many_pieces(gpu_lib):
+    """One KV head and two tiles on a 3,000-token context: fewer items than
+    resident workgroups, so every share holds one item and each tile is merged
+    from ~190 pieces."""
+    lay = small_varlen(520, dtype="bf16", num_heads=4, num_kv_heads=1, head_dim=128,
+                       prefill=((40, 3000),), decode_lens=())
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    out = _run(st, lay, "auto")
+    torch.cuda.synchronize()
+    want, _ = varlen_oracle(st, snap, req)
+    err = max_err(gpu_rows(out, "bf16"), want)
+    print(f"many pieces: max|err| = {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
+def test_prefill_stale_records_across_batches(gpu_lib):
+    """Batch A has prefill chunks first; batch B puts 20 decode rows at those
+    token positions and its chunk after them. B through A's workspace gives
+    the same bits as B through a fresh one, and matches the oracle."""
+    a_lay = small_varlen(530, dtype="bf16", num_heads=8, num_kv_heads=2,
+                         prefill=((120, 500), (64, 0)), decode_lens=(40,))
+    dec = list(range(30, 630, 30))
+    b_lay = build_layout("decode-then-chunk", "bf16", dec + [790], [1] * len(dec) + [90],
+                         num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, seed=531,
+                         pool_factor=1.3)
+    a = materialize(a_lay, "cuda")
+    gpu_write(a)
+    st, snap, req = prepare(b_lay)
+    gpu_write(st)
+    snap.apply_oracle_write(b_lay)
+    need = max(pa.pa_varlen_workspace_bytes(a.k_cache, a.v_cache, a_lay.num_seqs,
+                                            a.q.shape[0], 8, a.block_table.shape[1]),
+               pa.pa_varlen_workspace_bytes(st.k_cache, st.v_cache, b_lay.num_seqs,
+                                            st.q.shape[0], 8, st.block_table.shape[1]))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    _run(a, a_lay, ws)
+    stale = _run(st, b_lay, ws)
+    fresh = _run(st, b_lay, torch.zeros(need, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(stale.view(torch.int16), fresh.view(torch.int16))
+    want, _ = varlen_oracle(st, snap, req)
+    assert max_err(gpu_rows(stale, "bf16"), want) <= TOL["bf16"]
