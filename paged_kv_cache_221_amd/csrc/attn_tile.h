@@ -47,13 +47,17 @@ __device__ inline float xor_shuffle(float v, int mask) { return __shfl_xor(v, ma
 
 // max(v[l], v[l ^ 16]) and max(v[l], v[l ^ 32]) with the gfx950 row swaps
 // (VALU only: no LDS traffic, no lgkmcnt wait).
+// Maxima of scores use the IEEE-754-2019 maximum (NaN-propagating, one
+// v_maximum3_f32): fmaxf would make the compiler quiet both operands of every
+// lane exchange first. Scores are finite or -inf (masked).
+__device__ inline float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ inline float max_xor16(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float max_xor32(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float sum_xor16(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -592,7 +596,7 @@ __device__ inline void consume_block(RowState<D>& st, const typename Ops<E, D>::
     const int key = key0 + 4 * grp + i;
     s[i] = key < key_end ? acc[i] * scale_log2 : neg_inf();
   }
-  float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  float mx = fmax2(fmax2(s[0], s[1]), fmax2(s[2], s[3]));
   mx = max_xor16(mx);
   mx = max_xor32(mx);
   const float alpha = advance_max(st.m, mx);
@@ -612,7 +616,9 @@ __device__ inline void consume_block(RowState<D>& st, const typename Ops<E, D>::
 // scores, then every tile's softmax update, one combined rescale test, and
 // the block's PV operand built once for all tiles. Straight-line code, so
 // the tiles' independent MFMA and VALU chains interleave.
-template <class E, int D, int RT>
+// With MASK false every key of the block is visible to every valid row (the
+// caller has checked), and the per-key comparison is skipped.
+template <class E, int D, int RT, bool MASK = true>
 __device__ inline void consume_block_tiles(RowState<D> (&st)[RT], const typename Ops<E, D>::KV& kv,
                                            const typename Ops<E, D>::Q (&q)[RT], int key0,
                                            const int (&key_end)[RT], float scale_log2, int lane) {
@@ -630,9 +636,9 @@ __device__ inline void consume_block_tiles(RowState<D> (&st)[RT], const typename
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = key0 + 4 * grp + i;
-      s[i] = key < key_end[t] ? acc[t][i] * scale_log2 : neg_inf();
+      s[i] = (!MASK || key < key_end[t]) ? acc[t][i] * scale_log2 : neg_inf();
     }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    float mx = fmax2(fmax2(s[0], s[1]), fmax2(s[2], s[3]));
     mx = max_xor16(mx);
     mx = max_xor32(mx);
     alpha[t] = advance_max(st[t].m, mx);

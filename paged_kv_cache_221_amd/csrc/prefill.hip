@@ -21,6 +21,8 @@
 // kernel; a tile cut between shares is written as partials (normalised
 // output and log-sum-exp per piece) and renormalised by a small merge kernel
 // [P1 §07 LSE merge].
+#include <type_traits>
+
 #include "attn_tile.h"
 #include "pa_launch.h"
 
@@ -179,13 +181,23 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
 
   // keys at or past b1 * 16 belong to the next piece
   int kend[RT];
+  int kmin = 0x7fffffff;  // the fewest keys any valid row of this wave sees
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) kend[rt] = min(key_end[rt], b1 * kBlockTokens);
+  for (int rt = 0; rt < RT; ++rt) {
+    kend[rt] = min(key_end[rt], b1 * kBlockTokens);
+    const int tok = tok_base + (wave * RT + rt) * tpw + row / g;
+    if (row < tpw * g && tok < n) kmin = min(kmin, kend[rt]);
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) kmin = min(kmin, __shfl_xor(kmin, m, kWave));
+  // blocks before b_full are visible whole to every valid row: no mask
+  const int b_full = __builtin_amdgcn_readfirstlane(min(b1, kmin / kBlockTokens));
 
   typename St::Regs ring[RING];
 #pragma unroll
   for (int j = 0; j < RING; ++j) issue(ring[j], b0 + j);
-  for (int i0 = b0; i0 < b1; i0 += RING) {
+  // one group of RING blocks; the ring slot of block i is (i - b0) % RING
+  auto group = [&](int i0, auto masked) {
 #pragma unroll
     for (int j = 0; j < RING; ++j) {
       const int i = i0 + j;
@@ -200,9 +212,13 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
       // adds nothing, and the accumulators stay in one set of registers.
       typename O::KV kv;
       O::load_lds(kv, lds.k[buf], lds.v[buf], St::kLdsRow, lane);
-      consume_block_tiles<E, D, RT>(st, kv, q, i * kBlockTokens, kend, a.scale_log2, lane);
+      consume_block_tiles<E, D, RT, decltype(masked)::value>(st, kv, q, i * kBlockTokens, kend,
+                                                             a.scale_log2, lane);
     }
-  }
+  };
+  int i0 = b0;
+  for (; i0 + RING <= b_full; i0 += RING) group(i0, std::false_type{});
+  for (; i0 < b1; i0 += RING) group(i0, std::true_type{});
 
   // epilogue: normalise and store every valid row (partials when cut)
 #pragma unroll
