@@ -175,6 +175,27 @@ pa_status pa_decode_balanced(const pa_kv_cache *cache, void *out, const void *q,
                              int max_seq_len, float scale, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* A whole decode step in the two kernels of pa_decode_balanced: the KV write
+ * of pa_write_kv [P1 §02] fused in [P3 §1.4: the new token's K/V are
+ * appended, then used]. Request r has one new token (T = B): its rows
+ * k_new[r], v_new[r] go to slot slot_mapping[r] as pa_write_kv writes them
+ * (bit for bit, E4M3 quantisation included; a negative slot or one past the
+ * pool is skipped), and the workgroup that reads the request's last block
+ * writes them and uses them in registers as key/value position
+ * seq_lens[r] - 1. When every slot_mapping[r] >= 0 names that position
+ * (block_table[r][(L-1)/16] * 16 + (L-1) % 16 for L = seq_lens[r]), out and
+ * the cache are bit for bit those of pa_write_kv followed by
+ * pa_decode_balanced; other slots are written but not read back.
+ *   k_new, v_new  : [B, Hkv, D] (bf16 for an E4M3 cache, else cache->dtype)
+ *   slot_mapping  : int64 [B]
+ * Other arguments and the workspace as for pa_decode_balanced. */
+pa_status pa_write_decode_balanced(const pa_kv_cache *cache, void *out, const void *q,
+                                   const void *k_new, const void *v_new,
+                                   const int64_t *slot_mapping, const int32_t *block_table,
+                                   const int32_t *seq_lens, int num_seqs, int num_heads,
+                                   int max_blocks_per_seq, int max_seq_len, float scale,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Varlen mixed step [P1 §03/§04 flattened batch and cu_seqlens; P1 §07
  * chunked prefill]: request r owns query rows [cu[r], cu[r+1]) of the
  * flattened batch; n_r = cu[r+1] - cu[r] and its earlier context is

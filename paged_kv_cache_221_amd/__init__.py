@@ -21,5 +21,6 @@ from .api import (  # noqa: F401
     pa_status_str,
     pa_varlen,
     pa_varlen_workspace_bytes,
+    pa_write_decode_balanced,
     pa_write_kv,
 )

@@ -53,6 +53,8 @@ SIGNATURES = {
     "pa_decode_balanced_workspace_bytes": (ctypes.c_size_t, [_CACHE, _I, _I]),
     "pa_decode_balanced": (_I, [_CACHE, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, ctypes.c_size_t,
                                 _P]),
+    "pa_write_decode_balanced": (_I, [_CACHE, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P,
+                                      ctypes.c_size_t, _P]),
     "pa_copy_blocks": (_I, [_CACHE, _P, _I, _P]),
     "pa_rope_write_kv": (_I, [_CACHE, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "pa_bm_create": (_P, [_I, _I]),

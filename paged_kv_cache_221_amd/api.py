@@ -154,6 +154,39 @@ def pa_decode_balanced(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: 
     return out
 
 
+def pa_write_decode_balanced(k_cache, v_cache, q, k_new, v_new, slot_mapping, block_table,
+                             seq_lens, max_seq_len: int, scale: float, workspace=None, out=None,
+                             k_scale: float = 1.0, v_scale: float = 1.0):
+    """A decode step in one call: pa_write_kv of k_new/v_new [B, Hkv, D] to
+    slot_mapping [B] fused into pa_decode_balanced (see include/pa.h)."""
+    lib = _native.load()
+    c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
+    _dev(q, "q", _act_dtype(k_cache))
+    if q.dim() != 3 or q.shape[2] != c.head_dim:
+        raise ValueError("q must be [num_seqs, Hq, D]")
+    b, hq, _ = q.shape
+    max_blocks = _attention_meta(c, block_table, seq_lens, b)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    if tuple(slot_mapping.shape) != (b,):
+        raise ValueError("slot_mapping must be [num_seqs]")
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        _dev(x, name, _act_dtype(k_cache))
+        if tuple(x.shape) != (b, c.num_kv_heads, c.head_dim):
+            raise ValueError(f"{name} must be [num_seqs, Hkv, D]")
+    need = pa_decode_balanced_workspace_bytes(k_cache, v_cache, b, hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check("pa_write_decode_balanced", lib.pa_write_decode_balanced(
+        ctypes.byref(c), _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+        _ptr(block_table), _ptr(seq_lens), b, hq, max_blocks, int(max_seq_len), float(scale),
+        _ptr(workspace), workspace.numel(), _stream(q)))
+    return out
+
+
 def pa_splitk_num_splits(max_seq_len: int, split_tokens: int) -> int:
     return int(_native.load().pa_splitk_num_splits(int(max_seq_len), int(split_tokens)))
 

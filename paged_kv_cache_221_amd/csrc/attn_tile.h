@@ -157,6 +157,38 @@ struct Fp8 : Bf16 {
   using kv_storage = uint8_t;
 };
 
+// E4M3 code of an fp32 value: the nearest of the 8-bit float's values, ties
+// to the even code, magnitudes of 448 (the largest finite value) and more
+// saturating to 448, NaN kept (0x7f with the sign). Integer operations on the
+// fp32 bits: a normal result keeps 3 mantissa bits (a carry moves into the
+// exponent); below 2^-6 the values are the multiples of 2^-9.
+__device__ inline unsigned e4m3_code(float y) {
+  const unsigned u = __float_as_uint(y);
+  const unsigned sign = (u >> 24) & 0x80u;
+  const unsigned au = u & 0x7fffffffu;
+  if (au > 0x7f800000u) return sign | 0x7fu;
+  const float ay = __uint_as_float(au);
+  if (!(ay < 448.0f)) return sign | 0x7eu;
+  if (ay < 0.015625f) return sign | (unsigned)__builtin_rintf(ay * 512.0f);
+  const unsigned e = (au >> 23) - 120u;  // biased E4M3 exponent, 1 .. 15
+  const unsigned mant = au & 0x7fffffu;
+  unsigned r = mant >> 20;
+  const unsigned rem = mant & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+  return sign | min((e << 3) + r, 0x7eu);
+}
+
+// E4M3 codes of 4 bf16 values (two packed words, element 0 in the low half of
+// lo) divided by `scale` in fp32, as one word (element k in byte k): the
+// cache write's quantisation.
+__device__ inline unsigned bf16x4_to_fp8(unsigned lo, unsigned hi, float scale) {
+  const unsigned c0 = e4m3_code(__fdiv_rn(__uint_as_float(lo << 16), scale));
+  const unsigned c1 = e4m3_code(__fdiv_rn(__uint_as_float(lo & 0xffff0000u), scale));
+  const unsigned c2 = e4m3_code(__fdiv_rn(__uint_as_float(hi << 16), scale));
+  const unsigned c3 = e4m3_code(__fdiv_rn(__uint_as_float(hi & 0xffff0000u), scale));
+  return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+}
+
 // Four E4M3 codes (byte k of w is element k) -> four bf16, as two packed
 // words in the same order.
 __device__ inline void fp8x4_to_bf16(unsigned w, unsigned* lo, unsigned* hi) {
@@ -252,6 +284,55 @@ struct Ops16 {
   __device__ static void zero_v(KV& kv, int i) {
 #pragma unroll
     for (int w = 0; w < kVe / 2; ++w) kv.v[i].w[w] = 0u;
+  }
+  // A new key row and value row (one head, D elements each) in this lane's
+  // operand positions: nr.k as if the lane's key row were the new one, and
+  // every nr.v[i] the lane's columns of the new value row.
+  __device__ static void load_new(KV& nr, const void* k_row, const void* v_row, int lane,
+                                  float /*k_scale*/, float /*v_scale*/) {
+    const int m = lane & 15, grp = lane >> 4;
+    const uint16_t* kr = static_cast<const uint16_t*>(k_row);
+    const uint16_t* vr = static_cast<const uint16_t*>(v_row) + kVe * m;
+#pragma unroll
+    for (int c = 0; c < kQk; ++c) nr.k[c] = *reinterpret_cast<const u32x4*>(kr + 32 * c + 8 * grp);
+    VVec v;
+    if constexpr (kVe == 8) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(vr);
+      v.w[0] = t.x; v.w[1] = t.y; v.w[2] = t.z; v.w[3] = t.w;
+    } else {
+      const u32x2 t = *reinterpret_cast<const u32x2*>(vr);
+      v.w[0] = t.x; v.w[1] = t.y;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nr.v[i] = v;
+  }
+  // Replaces key/value row `row` of a loaded block by the new row.
+  __device__ static void patch(KV& kv, const KV& nr, int row, int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+    if (m == row) {
+#pragma unroll
+      for (int c = 0; c < kQk; ++c) kv.k[c] = nr.k[c];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * grp + i == row) kv.v[i] = nr.v[i];
+  }
+  // Stores the new rows (as held by load_new) to one head's cache rows.
+  __device__ static void store_new(const KV& nr, void* k_dst, void* v_dst, int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+    if (m == 0) {
+#pragma unroll
+      for (int c = 0; c < kQk; ++c)
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(k_dst) + 32 * c + 8 * grp) = nr.k[c];
+    }
+    if (grp == 0) {
+      uint16_t* vd = static_cast<uint16_t*>(v_dst) + kVe * m;
+      if constexpr (kVe == 8) {
+        *reinterpret_cast<u32x4*>(vd) = u32x4{nr.v[0].w[0], nr.v[0].w[1], nr.v[0].w[2], nr.v[0].w[3]};
+      } else {
+        *reinterpret_cast<u32x2*>(vd) = u32x2{nr.v[0].w[0], nr.v[0].w[1]};
+      }
+    }
   }
   __device__ static f32x4 scores(const KV& kv, const Q& q) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -382,6 +463,62 @@ struct Ops<Fp8, D> : Ops16<Bf16, D> {
   __device__ static void pv(f32x4 (&o)[Base::kChunks], const KV& kv, P p) {
     Base::pv_with(o, build_v(kv), p);
   }
+  // New rows arrive as bf16 and are quantised like the cache write.
+  __device__ static void load_new(KV& nr, const void* k_row, const void* v_row, int lane,
+                                  float k_scale, float v_scale) {
+    const int m = lane & 15, grp = lane >> 4;
+    const uint16_t* kr = static_cast<const uint16_t*>(k_row);
+    const uint16_t* vr = static_cast<const uint16_t*>(v_row) + kVe * m;
+#pragma unroll
+    for (int j = 0; j < kK16; ++j) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(kr + 16 * (grp + 4 * j));
+      const u32x4 b = *reinterpret_cast<const u32x4*>(kr + 16 * (grp + 4 * j) + 8);
+      nr.k[j] = u32x4{bf16x4_to_fp8(a.x, a.y, k_scale), bf16x4_to_fp8(a.z, a.w, k_scale),
+                      bf16x4_to_fp8(b.x, b.y, k_scale), bf16x4_to_fp8(b.z, b.w, k_scale)};
+    }
+    unsigned v[kVe / 4];
+    if constexpr (kVe == 8) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(vr);
+      v[0] = bf16x4_to_fp8(t.x, t.y, v_scale);
+      v[1] = bf16x4_to_fp8(t.z, t.w, v_scale);
+    } else {
+      const u32x2 t = *reinterpret_cast<const u32x2*>(vr);
+      v[0] = bf16x4_to_fp8(t.x, t.y, v_scale);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int w = 0; w < kVe / 4; ++w) nr.v[i][w] = v[w];
+  }
+  __device__ static void patch(KV& kv, const KV& nr, int row, int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+    if (m == row) {
+#pragma unroll
+      for (int j = 0; j < kK16; ++j) kv.k[j] = nr.k[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * grp + i == row) {
+#pragma unroll
+        for (int w = 0; w < kVe / 4; ++w) kv.v[i][w] = nr.v[i][w];
+      }
+  }
+  __device__ static void store_new(const KV& nr, void* k_dst, void* v_dst, int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+    if (m == 0) {
+#pragma unroll
+      for (int j = 0; j < kK16; ++j)
+        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(k_dst) + 16 * (grp + 4 * j)) = nr.k[j];
+    }
+    if (grp == 0) {
+      uint8_t* vd = static_cast<uint8_t*>(v_dst) + kVe * m;
+      if constexpr (kVe == 8) {
+        *reinterpret_cast<u32x2*>(vd) = u32x2{nr.v[0][0], nr.v[0][1]};
+      } else {
+        *reinterpret_cast<unsigned*>(vd) = nr.v[0][0];
+      }
+    }
+  }
 };
 
 // fp32 storage: QK and PV with 16x16x4 (one element per lane per MFMA).
@@ -455,6 +592,52 @@ struct Ops<F32, D> {
   __device__ static void zero_v(KV& kv, int i) {
 #pragma unroll
     for (int e = 0; e < kVe; ++e) kv.v[i][e] = 0.f;
+  }
+  __device__ static void load_new(KV& nr, const void* k_row, const void* v_row, int lane,
+                                  float /*k_scale*/, float /*v_scale*/) {
+    const int m = lane & 15, grp = lane >> 4;
+    const float* kr = static_cast<const float*>(k_row);
+    const float* vr = static_cast<const float*>(v_row) + kVe * m;
+#pragma unroll
+    for (int j = 0; j < kKv; ++j) nr.k[j] = *reinterpret_cast<const f32x4*>(kr + 16 * j + 4 * grp);
+    float v[kVe];
+#pragma unroll
+    for (int w = 0; w < kVe / 4; ++w) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(vr + 4 * w);
+      v[4 * w] = t.x; v[4 * w + 1] = t.y; v[4 * w + 2] = t.z; v[4 * w + 3] = t.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < kVe; ++e) nr.v[i][e] = v[e];
+  }
+  __device__ static void patch(KV& kv, const KV& nr, int row, int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+    if (m == row) {
+#pragma unroll
+      for (int j = 0; j < kKv; ++j) kv.k[j] = nr.k[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * grp + i == row) {
+#pragma unroll
+        for (int e = 0; e < kVe; ++e) kv.v[i][e] = nr.v[i][e];
+      }
+  }
+  __device__ static void store_new(const KV& nr, void* k_dst, void* v_dst, int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+    if (m == 0) {
+#pragma unroll
+      for (int j = 0; j < kKv; ++j)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(k_dst) + 16 * j + 4 * grp) = nr.k[j];
+    }
+    if (grp == 0) {
+      float* vd = static_cast<float*>(v_dst) + kVe * m;
+#pragma unroll
+      for (int w = 0; w < kVe / 4; ++w)
+        *reinterpret_cast<f32x4*>(vd + 4 * w) =
+            f32x4{nr.v[0][4 * w], nr.v[0][4 * w + 1], nr.v[0][4 * w + 2], nr.v[0][4 * w + 3]};
+    }
   }
   __device__ static f32x4 scores(const KV& kv, const Q& q) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -674,11 +857,17 @@ __device__ inline void consume_block_tiles(RowState<D> (&st)[RT], const typename
 // With SYNC, the workgroup meets at a barrier once per DEPTH blocks, so that
 // waves walking the same blocks (other heads) keep fetching them together;
 // every wave of the workgroup must then run the same number of blocks.
-template <class E, int D, int DEPTH, bool SYNC = false>
+// `patch(kv, i)` sees block i of the run after its loads and before it is
+// consumed (the fused decode step substitutes the new token's row there).
+struct NoPatch {
+  template <class KV>
+  __device__ void operator()(KV&, int) const {}
+};
+template <class E, int D, int DEPTH, bool SYNC = false, class Patch = NoPatch>
 __device__ inline void stream_blocks(RowState<D>& st, const typename Ops<E, D>::Q& q,
                                      const KvView<typename Ops<E, D>::kv_storage>& kv_view,
                                      int b_begin, int n, int key_end, int seq_len,
-                                     float scale_log2, int lane) {
+                                     float scale_log2, int lane, const Patch& patch = Patch{}) {
   using O = Ops<E, D>;
   using S = typename O::kv_storage;
   using KV = typename O::KV;
@@ -697,7 +886,8 @@ __device__ inline void stream_blocks(RowState<D>& st, const typename Ops<E, D>::
     const int64_t base = (int64_t)(ok ? pb : 0) * block_elems;
     O::load(kv, make_rsrc(kv_view.k + base, range), make_rsrc(kv_view.v + base, range), off);
   };
-  auto consume = [&](const KV& kv, int i) {
+  auto consume = [&](KV& kv, int i) {
+    patch(kv, i);
     consume_block<E, D>(st, kv, q, (b_begin + i) * kBlockTokens, i < n ? key_end : 0,
                         scale_log2, lane);
   };

@@ -117,6 +117,31 @@ __device__ inline bool single_tile(int n, int g) { return n >= 1 && n * g <= kTi
 // j + sg < T + segments, the per-head slot count.
 __device__ inline int64_t piece_slot(int64_t j, int64_t sg) { return j + sg; }
 
+// The fused write of request r's new rows (all KV heads) by one thread, for
+// requests without KV blocks, which no piece covers.
+template <class E, int D>
+__device__ inline void write_new_rows(const BalancedArgs& a, int r) {
+  using O = Ops<E, D>;
+  using S = typename O::storage;
+  using KS = typename O::kv_storage;
+  const int64_t slot = a.slot_mapping[r];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t rs = (int64_t)a.num_kv_heads * D;
+  const S* ks = static_cast<const S*>(a.k_new) + (int64_t)r * rs;
+  const S* vs = static_cast<const S*>(a.v_new) + (int64_t)r * rs;
+  KS* kd = static_cast<KS*>(const_cast<void*>(a.k_cache)) + slot * rs;
+  KS* vd = static_cast<KS*>(const_cast<void*>(a.v_cache)) + slot * rs;
+  for (int64_t e = 0; e < rs; ++e) {
+    if constexpr (sizeof(KS) == 1) {
+      kd[e] = (KS)e4m3_code(__fdiv_rn(__uint_as_float((unsigned)ks[e] << 16), a.k_scale));
+      vd[e] = (KS)e4m3_code(__fdiv_rn(__uint_as_float((unsigned)vs[e] << 16), a.v_scale));
+    } else {
+      kd[e] = ks[e];
+      vd[e] = vs[e];
+    }
+  }
+}
+
 template <class E, int D, int NW>
 __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel(const BalancedArgs a) {
   using O = Ops<E, D>;
@@ -163,6 +188,7 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
       S* dst = static_cast<S*>(a.out) + (int64_t)q_lo * a.num_heads * D;
       for (int64_t e = 0; e < (int64_t)n * a.num_heads * D; ++e) dst[e] = S(0);
       for (int k = 0; k < a.num_kv_heads; ++k) a.records[(int64_t)i * a.num_kv_heads + k] = int2{0, 0};
+      if (a.k_new != nullptr) write_new_rows<E, D>(a, i);
     }
   }
 
@@ -222,11 +248,30 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     const int64_t qrow = (int64_t)q_lo + (row_valid ? tok : 0);
     typename O::Q qop;
     O::load_q(qop, static_cast<const S*>(a.q) + (qrow * a.num_heads + head) * D, row_valid, lane);
+    // fused KV write: the piece holding the request's last block writes the
+    // new rows of its heads and uses them for that block's last key
+    int64_t slot = -1;
+    if (a.k_new != nullptr && b + len == nb)
+      slot = __builtin_amdgcn_readfirstlane(a.slot_mapping[r]);
+    const bool subst = slot >= 0 && slot < a.num_slots;
+    typename O::KV nr{};
+    if (subst) {
+      const int64_t src = ((int64_t)r * hkv + kvh) * D;
+      O::load_new(nr, static_cast<const S*>(a.k_new) + src, static_cast<const S*>(a.v_new) + src,
+                  lane, a.k_scale, a.v_scale);
+      const int64_t dst = slot * view.rs + (int64_t)kvh * D;
+      O::store_new(nr, static_cast<KS*>(const_cast<void*>(a.k_cache)) + dst,
+                   static_cast<KS*>(const_cast<void*>(a.v_cache)) + dst, lane);
+    }
+    const int new_row = (seq_len - 1) & (kBlockTokens - 1), new_blk = nb - 1 - b;
+    auto patch = [&](typename O::KV& kv, int i) {
+      if (subst && i == new_blk) O::patch(kv, nr, new_row, lane);
+    };
     RowState<D> st;
     st.init();
     // every wave of the workgroup walks the same blocks: same trip count
     stream_blocks<E, D, bal_depth<E>(), PA_BAL_SYNC != 0>(st, qop, view, b, len, key_end,
-                                                         seq_len, a.scale_log2, lane);
+                                                         seq_len, a.scale_log2, lane, patch);
     st.l = sum_xor16(st.l);
     st.l = sum_xor32(st.l);
 

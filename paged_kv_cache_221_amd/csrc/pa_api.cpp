@@ -189,6 +189,63 @@ VarlenLayout varlen_layout(int tw, pa_dtype dtype, int group, int head_dim, int 
   return l;
 }
 
+// pa_decode_balanced, with the decode step's KV write fused in when k_new
+// is given (pa_write_decode_balanced).
+pa_status decode_balanced(const pa_kv_cache* cache, void* out, const void* q, const void* k_new,
+                          const void* v_new, const int64_t* slot_mapping,
+                          const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
+                          int num_heads, int max_blocks_per_seq, int max_seq_len, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  s = check_attention_shape(cache, num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale);
+  if (s != PA_OK) return s;
+  if (num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (out == nullptr || q == nullptr || block_table == nullptr || seq_lens == nullptr)
+    return PA_ERR_NULL;
+  const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
+  if (tw <= 0) return PA_ERR_LAUNCH;
+  const int group = num_heads / cache->num_kv_heads;
+  const BalancedLayout lay =
+      balanced_layout(tw, group, cache->head_dim, num_seqs, cache->num_kv_heads);
+  if (workspace == nullptr) return PA_ERR_NULL;
+  if (group > pa::kTileRows) return PA_ERR_UNSUPPORTED;
+  if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  pa::BalancedArgs a{};
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.q = q;
+  a.out = out;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+  a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
+  a.records = reinterpret_cast<int2*>(ws + lay.records);
+  a.cu_seqlens = nullptr;
+  a.num_tokens = num_seqs;
+  a.causal = 0;
+  a.slot_rows = group;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = group;
+  a.head_dim = cache->head_dim;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.total_waves = tw;
+  a.scale_log2 = scale_log2_of(cache, scale);
+  a.out_scale = out_scale_of(cache);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.num_slots = (int64_t)cache->num_blocks * cache->block_size;
+  a.k_scale = cache->dtype == PA_FP8_E4M3 ? cache->k_scale : 1.f;
+  a.v_scale = cache->dtype == PA_FP8_E4M3 ? cache->v_scale : 1.f;
+  return launched(pa::launch_balanced(a, cache->dtype, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -460,48 +517,23 @@ pa_status pa_decode_balanced(const pa_kv_cache* cache, void* out, const void* q,
                              const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
                              int num_heads, int max_blocks_per_seq, int max_seq_len, float scale,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  pa_status s = check_cache(cache);
-  if (s != PA_OK) return s;
-  s = check_attention_shape(cache, num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale);
-  if (s != PA_OK) return s;
-  if (num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
-  if (out == nullptr || q == nullptr || block_table == nullptr || seq_lens == nullptr)
+  return decode_balanced(cache, out, q, nullptr, nullptr, nullptr, block_table, seq_lens,
+                         num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale, workspace,
+                         workspace_bytes, stream);
+}
+
+pa_status pa_write_decode_balanced(const pa_kv_cache* cache, void* out, const void* q,
+                                   const void* k_new, const void* v_new,
+                                   const int64_t* slot_mapping, const int32_t* block_table,
+                                   const int32_t* seq_lens, int num_seqs, int num_heads,
+                                   int max_blocks_per_seq, int max_seq_len, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (cache != nullptr && num_seqs > 0 &&
+      (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr))
     return PA_ERR_NULL;
-  const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
-  if (tw <= 0) return PA_ERR_LAUNCH;
-  const int group = num_heads / cache->num_kv_heads;
-  const BalancedLayout lay =
-      balanced_layout(tw, group, cache->head_dim, num_seqs, cache->num_kv_heads);
-  if (workspace == nullptr) return PA_ERR_NULL;
-  if (group > pa::kTileRows) return PA_ERR_UNSUPPORTED;
-  if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  pa::BalancedArgs a{};
-  a.k_cache = cache->k_cache;
-  a.v_cache = cache->v_cache;
-  a.q = q;
-  a.out = out;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
-  a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
-  a.records = reinterpret_cast<int2*>(ws + lay.records);
-  a.cu_seqlens = nullptr;
-  a.num_tokens = num_seqs;
-  a.causal = 0;
-  a.slot_rows = group;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.group = group;
-  a.head_dim = cache->head_dim;
-  a.num_blocks = cache->num_blocks;
-  a.max_blocks = max_blocks_per_seq;
-  a.total_waves = tw;
-  a.scale_log2 = scale_log2_of(cache, scale);
-  a.out_scale = out_scale_of(cache);
-  return launched(pa::launch_balanced(a, cache->dtype, static_cast<hipStream_t>(stream)));
+  return decode_balanced(cache, out, q, k_new, v_new, slot_mapping, block_table, seq_lens,
+                         num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale, workspace,
+                         workspace_bytes, stream);
 }
 
 }  // extern "C"

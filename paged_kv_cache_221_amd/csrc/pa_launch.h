@@ -99,6 +99,16 @@ struct BalancedArgs {
   int total_waves;
   float scale_log2;          // scale * log2(e) (times the K scale of an E4M3 cache)
   float out_scale;           // output factor: the V scale of an E4M3 cache, else 1
+  // Fused KV write of a decode step (nullptr k_new: none): request r's new
+  // rows k_new/v_new [B, Hkv, D] (bf16 for an E4M3 cache) go to slot
+  // slot_mapping[r] when 0 <= slot < num_slots, and stand in for key/value
+  // position seq_len - 1 of the request.
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slot_mapping;
+  int64_t num_slots;
+  float k_scale;             // E4M3 quantisation scales of the write
+  float v_scale;
 };
 
 // Waves per workgroup the attention kernel is built for.

@@ -36,27 +36,6 @@ __global__ __launch_bounds__(kWriteThreads) void write_kv_kernel(
   }
 }
 
-// E4M3 code of an fp32 value: the nearest of the 8-bit float's values, ties
-// to the even code, magnitudes of 448 (the largest finite value) and more
-// saturating to 448, NaN kept (0x7f with the sign). Integer operations on the
-// fp32 bits: a normal result keeps 3 mantissa bits (a carry moves into the
-// exponent); below 2^-6 the values are the multiples of 2^-9.
-__device__ inline unsigned e4m3_code(float y) {
-  const unsigned u = __float_as_uint(y);
-  const unsigned sign = (u >> 24) & 0x80u;
-  const unsigned au = u & 0x7fffffffu;
-  if (au > 0x7f800000u) return sign | 0x7fu;
-  const float ay = __uint_as_float(au);
-  if (!(ay < 448.0f)) return sign | 0x7eu;
-  if (ay < 0.015625f) return sign | (unsigned)__builtin_rintf(ay * 512.0f);
-  const unsigned e = (au >> 23) - 120u;  // biased E4M3 exponent, 1 .. 15
-  const unsigned mant = au & 0x7fffffu;
-  unsigned r = mant >> 20;
-  const unsigned rem = mant & 0xfffffu;
-  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
-  return sign | min((e << 3) + r, 0x7eu);
-}
-
 // KV write into an E4M3 cache: bf16 rows in, each element divided by the
 // cache's scale (fp32, correctly rounded) and stored as its E4M3 code. Each
 // thread converts 8 elements (16 bytes in, 8 bytes out).
