@@ -285,6 +285,11 @@ struct Ops16 {
 #pragma unroll
     for (int w = 0; w < kVe / 2; ++w) kv.v[i].w[w] = 0u;
   }
+  // q -> -q (sign bits flipped: exact)
+  __device__ static void negate_q(Q& q) {
+#pragma unroll
+    for (int c = 0; c < kQk; ++c) q.q[c] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
   // A new key row and value row (one head, D elements each) in this lane's
   // operand positions: nr.k as if the lane's key row were the new one, and
   // every nr.v[i] the lane's columns of the new value row.
@@ -593,6 +598,10 @@ struct Ops<F32, D> {
 #pragma unroll
     for (int e = 0; e < kVe; ++e) kv.v[i][e] = 0.f;
   }
+  __device__ static void negate_q(Q& q) {
+#pragma unroll
+    for (int j = 0; j < kKv; ++j) q.q[j] = -q.q[j];
+  }
   __device__ static void load_new(KV& nr, const void* k_row, const void* v_row, int lane,
                                   float /*k_scale*/, float /*v_scale*/) {
     const int m = lane & 15, grp = lane >> 4;
@@ -800,7 +809,8 @@ __device__ inline void consume_block(RowState<D>& st, const typename Ops<E, D>::
 // the block's PV operand built once for all tiles. Straight-line code, so
 // the tiles' independent MFMA and VALU chains interleave.
 // With MASK false every key of the block is visible to every valid row (the
-// caller has checked), and the per-key comparison is skipped.
+// caller has checked), the per-key comparison is skipped, and scale_log2
+// must be >= 0 (a caller with a negative scale negates q instead).
 template <class E, int D, int RT, bool MASK = true>
 __device__ inline void consume_block_tiles(RowState<D> (&st)[RT], const typename Ops<E, D>::KV& kv,
                                            const typename Ops<E, D>::Q (&q)[RT], int key0,
@@ -815,21 +825,35 @@ __device__ inline void consume_block_tiles(RowState<D> (&st)[RT], const typename
   bool moved = false;
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
-    float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = key0 + 4 * grp + i;
-      s[i] = (!MASK || key < key_end[t]) ? acc[t][i] * scale_log2 : neg_inf();
-    }
-    float mx = fmax2(fmax2(s[0], s[1]), fmax2(s[2], s[3]));
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
-    alpha[t] = advance_max(st[t].m, mx);
-    moved = moved || alpha[t] != 1.0f;
-    const float m_use = st[t].m == neg_inf() ? 0.f : st[t].m;
     float p[4];
+    if constexpr (MASK) {
+      float s[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - m_use);
+      for (int i = 0; i < 4; ++i) {
+        const int key = key0 + 4 * grp + i;
+        s[i] = key < key_end[t] ? acc[t][i] * scale_log2 : neg_inf();
+      }
+      float mx = fmax2(fmax2(s[0], s[1]), fmax2(s[2], s[3]));
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);
+      alpha[t] = advance_max(st[t].m, mx);
+      const float m_use = st[t].m == neg_inf() ? 0.f : st[t].m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - m_use);
+    } else {
+      // every key visible and scale_log2 >= 0: the row maximum of the scaled
+      // scores is the scaled maximum of the raw ones (rounding is monotonic),
+      // the reference is finite once the block is taken in, and each
+      // exponent is one fused multiply-add
+      float mx = fmax2(fmax2(acc[t][0], acc[t][1]), fmax2(acc[t][2], acc[t][3]));
+      mx = max_xor16(mx);
+      mx = max_xor32(mx) * scale_log2;
+      alpha[t] = advance_max(st[t].m, mx);
+      const float neg_m = -st[t].m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(acc[t][i], scale_log2, neg_m));
+    }
+    moved = moved || alpha[t] != 1.0f;
     st[t].l = st[t].l * alpha[t] + ((p[0] + p[1]) + (p[2] + p[3]));
     pk[t] = O::pack_p(p);
   }

@@ -179,6 +179,15 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
     }
   };
 
+  // a negative softmax scale is applied as a positive one to -q (exact), as
+  // the unmasked blocks need
+  const bool neg = a.scale_log2 < 0.f;
+  const float scale_log2 = neg ? -a.scale_log2 : a.scale_log2;
+  if (neg) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) O::negate_q(q[rt]);
+  }
+
   // keys at or past b1 * 16 belong to the next piece
   int kend[RT];
   int kmin = 0x7fffffff;  // the fewest keys any valid row of this wave sees
@@ -213,7 +222,7 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
       typename O::KV kv;
       O::load_lds(kv, lds.k[buf], lds.v[buf], St::kLdsRow, lane);
       consume_block_tiles<E, D, RT, decltype(masked)::value>(st, kv, q, i * kBlockTokens, kend,
-                                                             a.scale_log2, lane);
+                                                             scale_log2, lane);
     }
   };
   int i0 = b0;

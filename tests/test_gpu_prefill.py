@@ -91,3 +91,27 @@ def test_prefill_stale_records_across_batches(gpu_lib):
     assert torch.equal(stale.view(torch.int16), fresh.view(torch.int16))
     want, _ = varlen_oracle(st, snap, req)
     assert max_err(gpu_rows(stale, "bf16"), want) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("scale_factor", [-1.0, 0.0])
+def test_prefill_negative_and_zero_scale(gpu_lib, scale_factor):
+    """Blocks every row sees whole take the scale inside a fused multiply-add
+    after a max over raw scores, which needs a non-negative scale: a negative
+    one is applied to -q instead; zero gives the mean of the visible values."""
+    import oracle
+    lay = small_varlen(540, dtype="bf16", num_heads=8, num_kv_heads=2, head_dim=128,
+                       prefill=((70, 200), (33, 0)), decode_lens=(1, 90))
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    scale = scale_factor * lay.scale
+    for ws in ("auto", None):
+        out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                           st.block_table, lay.max_query_len, lay.max_seq_len, scale,
+                           workspace=ws)
+        torch.cuda.synchronize()
+        want, _ = oracle.paged_varlen(snap.q, snap.k, snap.v, lay.cu_seqlens_q, lay.seq_lens,
+                                      lay.block_table, scale, lay.block_size, "bf16")
+        err = max_err(gpu_rows(out, "bf16"), want)
+        print(f"scale {scale:+.4f} workspace={ws}: max|err| = {err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
