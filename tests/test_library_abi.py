@@ -124,3 +124,20 @@ def test_e4m3_cache_validation(lib):
     assert lib.pa_rope_write_kv(byref(c), one, 8, one, one, one, one, one, 128, 128, 1, 4,
                                 None) == -4
     assert lib.pa_lse_merge(one, None, one, one, one, 1, 8, 128, 64, 32, 3, None) == -3
+
+
+def test_fused_decode_step_validation(lib):
+    """pa_write_decode_balanced needs the new rows and slots (NULL -> -1);
+    zero requests is a no-op."""
+    byref = ctypes.byref
+    one = ctypes.c_void_p(1)
+    c = _cache()
+    assert lib.pa_write_decode_balanced(byref(c), one, one, None, one, one, one, one, 1, 8, 4,
+                                        64, 0.1, one, 1 << 20, None) == -1
+    assert lib.pa_write_decode_balanced(byref(c), one, one, one, one, None, one, one, 1, 8, 4,
+                                        64, 0.1, one, 1 << 20, None) == -1
+    assert lib.pa_write_decode_balanced(byref(c), None, None, None, None, None, None, None, 0, 8,
+                                        4, 64, 0.1, None, 0, None) == 0
+    # the attention checks still apply: heads not a multiple of KV heads
+    assert lib.pa_write_decode_balanced(byref(c), one, one, one, one, one, one, one, 1, 7, 4,
+                                        64, 0.1, one, 1 << 20, None) == -2
