@@ -255,8 +255,15 @@ def cpu_baseline(st, layout, budget_s: float):
                       f"with BLAS on {threads} threads; host cpu_count={os.cpu_count()}"}
 
 
-def secondary(args):
-    """Per-config attention timings on the other step shapes (not the metric)."""
+SECONDARY_LEGS = ("long-context-splitk-bf16", "llama2-7b-mha-decode-fp16", "mixed-step-bf16",
+                  "mixed-step-prefill-chunks-bf16", "llama3-8b-decode-e4m3-cache",
+                  "rope-write-kv-mixed-step-bf16", "copy-on-write-blocks-bf16",
+                  "block-manager-host")
+
+
+def secondary(args, only=None):
+    """Per-config attention timings on the other step shapes (not the metric);
+    with ``only``, just that leg (for profiling one workload)."""
     import torch
     import paged_kv_cache_221_amd as pa
     from workloads import llama2_7b_mha_decode, long_context_splitk, mixed_step
@@ -266,6 +273,8 @@ def secondary(args):
     for name, fn in (("long-context-splitk-bf16", long_context_splitk),
                      ("llama2-7b-mha-decode-fp16", llama2_7b_mha_decode),
                      ("mixed-step-bf16", mixed_step)):
+        if only is not None and name != only:
+            continue
         lay = fn()
         st = materialize(lay, "cuda", poison=False)
         if name.startswith("long"):
@@ -303,11 +312,14 @@ def secondary(args):
         print(f"[bench] {name}: attention {kern:.4f} ms", file=sys.stderr, flush=True)
         del st, step
         torch.cuda.empty_cache()
-    res["mixed-step-prefill-chunks-bf16"] = bench_prefill_only(k)
-    res["llama3-8b-decode-e4m3-cache"] = bench_fp8_decode(k)
-    res["rope-write-kv-mixed-step-bf16"] = bench_rope_write(k)
-    res["copy-on-write-blocks-bf16"] = bench_copy_blocks(k)
-    res["block-manager-host"] = bench_block_manager()
+    for name, leg in (("mixed-step-prefill-chunks-bf16", bench_prefill_only),
+                      ("llama3-8b-decode-e4m3-cache", bench_fp8_decode),
+                      ("rope-write-kv-mixed-step-bf16", bench_rope_write),
+                      ("copy-on-write-blocks-bf16", bench_copy_blocks)):
+        if only is None or name == only:
+            res[name] = leg(k)
+    if only is None or only == "block-manager-host":
+        res["block-manager-host"] = bench_block_manager()
     return res
 
 
@@ -496,6 +508,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--only", choices=SECONDARY_LEGS, default=None,
+                    help="run only this secondary workload and print its line (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run torch's elementwise negation over this many MiB of "
                          "fp32 (3 times): a kernel that reads and writes a known number of "
@@ -529,6 +543,9 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.only is not None:
+        print(json.dumps({"secondary": secondary(args, args.only)}), flush=True)
+        return
 
     layout = llama3_8b_decode()
     copies = [materialize(layout, "cuda", seed_offset=i) for i in range(args.copies)]
