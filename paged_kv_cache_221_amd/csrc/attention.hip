@@ -4,9 +4,9 @@
 // One workgroup works on one (query tile, request, KV head, KV split).
 // - A request whose query rows times the GQA group fit one 16-row tile
 //   (decode, [P1 §04 table]: query_len 1; also short multi-token queries)
-//   is a "single-tile" unit: the waves of the workgroup take interleaved KV
-//   blocks of the split and their partial softmax states are merged through
-//   LDS at the end. Decode streams the whole KV from HBM, so this is the
+//   is a "single-tile" unit: the waves of the workgroup take contiguous runs
+//   of the split's KV blocks and their partial softmax states are merged
+//   through LDS at the end. Decode streams the whole KV from HBM, so this is the
 //   bandwidth-bound path ([P1 §04], [P3 §1.2]).
 // - A longer query (chunked prefill, [P1 §07]) is left to prefill.hip.
 // Split-K (Flash-Decoding, [P1 §07]) writes each split's normalised output

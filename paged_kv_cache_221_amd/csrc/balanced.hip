@@ -24,6 +24,11 @@
 // (Merging inside this kernel would need device-scope fences, which write
 // back and invalidate a whole L2 per piece and cost far more than the extra
 // launch.)
+//
+// Given new K/V rows (the fused decode step [P1 §02 slot_mapping write]),
+// the piece holding a request's last block also stores the request's new
+// rows of its heads to their slot and substitutes them, in registers, for
+// key position seq_len - 1, so the write and the read need no ordering.
 #include "attn_tile.h"
 #include "pa_launch.h"
 

@@ -3,7 +3,8 @@
 //
 // Each new token's K row and V row (Hkv * D elements each, contiguous in both
 // the input and the cache) is copied into the slot slot_mapping names, as
-// raw 16-byte vectors: the write is a bit-exact copy whatever the dtype.
+// raw 16-byte vectors: the write is a bit-exact copy whatever the dtype (an
+// E4M3 cache instead stores the quantised codes of bf16 rows [P3 §4.1]).
 // One workgroup per token; its threads stride over the K then the V vectors.
 // The block copy moves whole blocks (block_size token rows) the same way,
 // one workgroup per (source, destination) pair. The rotary-embedding variant
