@@ -12,7 +12,7 @@
  *        block table, copy-on-write sharing, where the block table lives.
  *   [P3] the LLM inference-optimisation survey at adg.csdn.net
  *        (695256bb5b9f5f31781b99f3): 1.4 KV cache, 1.5 memory, 3.3 GQA,
- *        3.4 FlashAttention, 3.5 PageAttention.
+ *        3.4 FlashAttention, 3.5 PageAttention, 4.1 quantisation.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -42,7 +42,8 @@
  *   Hq / Hkv <= 16; fp32, fp16 and bf16 storage with fp32 accumulation, and
  *   E4M3 KV caches (bf16 arithmetic on the exactly widened codes) in
  *   pa_write_kv, pa_copy_blocks, pa_decode, pa_decode_splitk,
- *   pa_decode_balanced and pa_varlen batches without prefill chunks.
+ *   pa_decode_balanced, pa_write_decode_balanced and pa_varlen batches
+ *   without prefill chunks.
  *   Anything else returns PA_ERR_UNSUPPORTED.
  */
 #ifndef PA_H
