@@ -45,7 +45,7 @@ namespace {
 #define PA_BAL_DEPTH 2
 #endif
 #ifndef PA_BAL_FP8_DEPTH
-#define PA_BAL_FP8_DEPTH 3
+#define PA_BAL_FP8_DEPTH 2
 #endif
 // Whether the head waves of a workgroup meet at a barrier every DEPTH blocks.
 #ifndef PA_BAL_SYNC

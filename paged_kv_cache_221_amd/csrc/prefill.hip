@@ -8,8 +8,10 @@
 // of one (request, KV head); every KV block is fetched once per workgroup into
 // double-buffered LDS through a register prefetch ring of PA_PREFILL_RING
 // blocks, and each wave reads the block's MFMA operands from LDS once and
-// applies them to all of its RT row tiles. Scores and probabilities stay in
-// registers (the FlashAttention principle [P3 §3.4]).
+// applies them to all of its RT row tiles. 16-bit operands are staged and
+// consumed two blocks at a time, so that P.V runs as full-rate 16x16x32
+// products. Scores and probabilities stay in registers (the FlashAttention
+// principle [P3 §3.4]).
 //
 // A workgroup's time is its tile's key count, which in a causal chunk grows
 // with the tile's position and with the request's cached context: one
@@ -97,11 +99,22 @@ __device__ inline int pf_tile_blocks(const AttnArgs& a, const PfRequest& q, int 
   return (kmax + kBlockTokens - 1) / kBlockTokens;
 }
 
-// Double-buffered LDS copies of one KV block's head slice.
+// 16-bit operands are consumed two blocks at a time (consume_pair_tiles)
+// unless PA_PREFILL_PAIRS is 0; fp32 ones block by block.
+#ifndef PA_PREFILL_PAIRS
+#define PA_PREFILL_PAIRS 1
+#endif
+template <class E>
+constexpr bool pf_pairs() {
+  return PA_PREFILL_PAIRS && sizeof(typename E::storage) == 2;
+}
+// Double-buffered LDS copies of the KV blocks' head slices consumed at once
+// (a pair or one block).
 template <class E, int D>
 struct PfLds {
-  char k[2][kBlockTokens * Stage<E, D>::kLdsRow];
-  char v[2][kBlockTokens * Stage<E, D>::kLdsRow];
+  static constexpr int kBufs = pf_pairs<E>() ? 4 : 2;
+  char k[kBufs][kBlockTokens * Stage<E, D>::kLdsRow];
+  char v[kBufs][kBlockTokens * Stage<E, D>::kLdsRow];
 };
 
 // One piece: KV blocks [b0, b1) of tile `tile` of request r (rq) for KV
@@ -205,24 +218,46 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
   typename St::Regs ring[RING];
 #pragma unroll
   for (int j = 0; j < RING; ++j) issue(ring[j], b0 + j);
-  // one group of RING blocks; the ring slot of block i is (i - b0) % RING
+  // One group of RING blocks; the ring slot of block i is (i - b0) % RING.
+  // Blocks are consumed unconditionally, like the loads: a padding block at
+  // or past b1 was read as zeros and its keys are past every row's limit
+  // (kend), so it adds nothing, and the accumulators stay in one set of
+  // registers.
   auto group = [&](int i0, auto masked) {
+    if constexpr (pf_pairs<E>()) {
+      static_assert(RING % 4 == 0, "pairs alternate between two LDS buffer pairs");
 #pragma unroll
-    for (int j = 0; j < RING; ++j) {
-      const int i = i0 + j;
-      const int buf = j & 1;
-      stage(ring[j], buf);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      issue(ring[j], i + RING);
-      __builtin_amdgcn_sched_barrier(0);
-      // Unconditional, like the loads: a padding block at or past b1 was
-      // read as zeros and its keys are past every row's limit (kend), so it
-      // adds nothing, and the accumulators stay in one set of registers.
-      typename O::KV kv;
-      O::load_lds(kv, lds.k[buf], lds.v[buf], St::kLdsRow, lane);
-      consume_block_tiles<E, D, RT, decltype(masked)::value>(st, kv, q, i * kBlockTokens, kend,
-                                                             scale_log2, lane);
+      for (int j = 0; j < RING; j += 2) {
+        const int i = i0 + j;
+        const int b = j & 2;  // this pair's buffers: b, b + 1
+        stage(ring[j], b);
+        stage(ring[j + 1], b + 1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(ring[j], i + RING);
+        issue(ring[j + 1], i + 1 + RING);
+        __builtin_amdgcn_sched_barrier(0);
+        typename O::KV kv0, kv1;
+        O::load_lds(kv0, lds.k[b], lds.v[b], St::kLdsRow, lane);
+        O::load_lds(kv1, lds.k[b + 1], lds.v[b + 1], St::kLdsRow, lane);
+        consume_pair_tiles<E, D, RT, decltype(masked)::value>(st, kv0, kv1, q, i * kBlockTokens,
+                                                              kend, scale_log2, lane);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RING; ++j) {
+        const int i = i0 + j;
+        const int buf = j & 1;
+        stage(ring[j], buf);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(ring[j], i + RING);
+        __builtin_amdgcn_sched_barrier(0);
+        typename O::KV kv;
+        O::load_lds(kv, lds.k[buf], lds.v[buf], St::kLdsRow, lane);
+        consume_block_tiles<E, D, RT, decltype(masked)::value>(st, kv, q, i * kBlockTokens, kend,
+                                                               scale_log2, lane);
+      }
     }
   };
   int i0 = b0;
