@@ -23,6 +23,7 @@
 // kernel; a tile cut between shares is written as partials (normalised
 // output and log-sum-exp per piece) and renormalised by a small merge kernel
 // [P1 §07 LSE merge].
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_tile.h"
@@ -476,12 +477,15 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_share
 
 // Renormalises the cut tiles of the equal-share prefill [P1 §07 LSE merge]:
 // one wave per (query token, KV head), its g heads side by side (lph lanes
-// per head, D / lph >= 4 dims per lane). The token's record names its tile's
-// first partial slot s0 and piece count c (0: nothing to merge); piece p > 0
-// sits at slot 2 (s0 / 2 + p), the first piece of each later share. Pieces
-// are folded in with a running maximum, so their loads do not wait for each
-// other. A record naming slots past the workspace is ignored.
-template <class E>
+// per head, DPL = D / lph >= 4 dims per lane). The token's record names its
+// tile's first partial slot s0 and piece count c (0: nothing to merge); piece
+// p > 0 sits at slot 2 (s0 / 2 + p), the first piece of each later share. The
+// loads of kPieceBatch pieces are issued together and then folded in with a
+// running maximum, so a tile of up to kPieceBatch pieces costs two dependent
+// memory round trips (record, then pieces). A record naming slots past the
+// workspace is ignored.
+constexpr int kPieceBatch = 4;
+template <class E, int DPL>
 __global__ __launch_bounds__(4 * kWave) void prefill_share_merge_kernel(const AttnArgs a,
                                                                         int pf_rows, int D) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -492,41 +496,49 @@ __global__ __launch_bounds__(4 * kWave) void prefill_share_merge_kernel(const At
   const int64_t slots = 2 * (int64_t)a.pf_shares;
   if (cnt <= 0 || s0 < 0 || s0 >= slots || 2 * ((int64_t)(s0 >> 1) + cnt - 1) >= slots) return;
   const int g = a.group;
-  int gp = 1;
-  while (gp < g) gp <<= 1;
-  const int lph = min(kWave / gp, D / 4);  // lanes per head
+  const int lph = D / DPL;  // lanes per head
   const int hh = lane / lph;
   if (hh >= g) return;
-  const int dpl = D / lph;                 // dims per lane: 4 .. 32 for g <= 16
-  const int d0 = (lane % lph) * dpl;
+  const int d0 = (lane % lph) * DPL;
   const int64_t prow = rec.z + hh;
-  constexpr int kMaxDpl = 32;
-  float acc[kMaxDpl];
+  float acc[DPL];
 #pragma unroll
-  for (int i = 0; i < kMaxDpl; ++i) acc[i] = 0.f;
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
   float m = neg_inf(), l = 0.f;
-  for (int p = 0; p < cnt; ++p) {
-    const int64_t sr = (p == 0 ? s0 : 2 * ((int64_t)(s0 >> 1) + p)) * pf_rows + prow;
-    const float lse = a.pf_lse[sr];
-    const float* o = a.pf_o + sr * D + d0;
-    float v[kMaxDpl];
+  for (int p0 = 0; p0 < cnt; p0 += kPieceBatch) {
+    float lse[kPieceBatch];
+    float v[kPieceBatch][DPL];
 #pragma unroll
-    for (int i = 0; i < kMaxDpl; i += 4) {
-      if (i < dpl) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(o + i);
-        v[i] = x[0];
-        v[i + 1] = x[1];
-        v[i + 2] = x[2];
-        v[i + 3] = x[3];
+    for (int k = 0; k < kPieceBatch; ++k) {
+      const int p = p0 + k;
+      const bool ok = p < cnt;
+      const int64_t sr = (p == 0 ? s0 : 2 * ((int64_t)(s0 >> 1) + p)) * pf_rows + prow;
+      lse[k] = ok ? a.pf_lse[sr] : neg_inf();
+      const float* o = a.pf_o + (ok ? sr : 0) * D + d0;
+#pragma unroll
+      for (int i = 0; i < DPL; i += 4) {
+        const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(o + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+        v[k][i] = x[0];
+        v[k][i + 1] = x[1];
+        v[k][i + 2] = x[2];
+        v[k][i + 3] = x[3];
       }
     }
-    const float mn = fmaxf(m, lse);
-    if (mn == neg_inf()) continue;     // no piece with keys yet
-    const float alpha = fast_exp2(m - mn), w = fast_exp2(lse - mn);
+    float mn = m;
 #pragma unroll
-    for (int i = 0; i < kMaxDpl; ++i)
-      if (i < dpl) acc[i] = acc[i] * alpha + w * v[i];
-    l = l * alpha + w;
+    for (int k = 0; k < kPieceBatch; ++k) mn = fmaxf(mn, lse[k]);
+    if (mn == neg_inf()) continue;  // no piece with keys yet
+    const float alpha = fast_exp2(m - mn);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] *= alpha;
+    l *= alpha;
+#pragma unroll
+    for (int k = 0; k < kPieceBatch; ++k) {
+      const float w = fast_exp2(lse[k] - mn);  // 0 for a piece without keys or past cnt
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] += w * v[k][i];
+      l += w;
+    }
     m = mn;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -534,13 +546,11 @@ __global__ __launch_bounds__(4 * kWave) void prefill_share_merge_kernel(const At
   const int token = (int)(unit / a.num_kv_heads), kvh = (int)(unit - (int64_t)token * a.num_kv_heads);
   S* out = static_cast<S*>(a.out) + ((int64_t)token * a.num_heads + kvh * g + hh) * D + d0;
 #pragma unroll
-  for (int i = 0; i < kMaxDpl; ++i) {
-    if (i < dpl) {
-      if constexpr (sizeof(S) == 2) {
-        out[i] = E::from_float(acc[i] * inv);
-      } else {
-        out[i] = acc[i] * inv;
-      }
+  for (int i = 0; i < DPL; ++i) {
+    if constexpr (sizeof(S) == 2) {
+      out[i] = E::from_float(acc[i] * inv);
+    } else {
+      out[i] = acc[i] * inv;
     }
   }
 }
@@ -627,13 +637,25 @@ hipError_t launch_prefill_merge(const AttnArgs& a, pa_dtype dtype, int head_dim,
   const int64_t units = (int64_t)a.num_tokens * a.num_kv_heads;
   if (units <= 0 || a.pf_shares <= 0) return hipSuccess;
   const int rows = prefill_rows(dtype);
+  int gp = 1;
+  while (gp < a.group) gp <<= 1;
+  const int dpl = head_dim / std::min(kWave / gp, head_dim / 4);  // 4 .. 32 for group <= 16
   const dim3 grid((unsigned)((units + 3) / 4)), block(4 * kWave);
+#define PA_PF_MERGE(E)                                                                             \
+  switch (dpl) {                                                                                   \
+    case 4: prefill_share_merge_kernel<E, 4><<<grid, block, 0, stream>>>(a, rows, head_dim); break;   \
+    case 8: prefill_share_merge_kernel<E, 8><<<grid, block, 0, stream>>>(a, rows, head_dim); break;   \
+    case 16: prefill_share_merge_kernel<E, 16><<<grid, block, 0, stream>>>(a, rows, head_dim); break; \
+    case 32: prefill_share_merge_kernel<E, 32><<<grid, block, 0, stream>>>(a, rows, head_dim); break; \
+    default: return hipErrorInvalidValue;                                                          \
+  }
   switch (dtype) {
-    case PA_BF16: prefill_share_merge_kernel<Bf16><<<grid, block, 0, stream>>>(a, rows, head_dim); break;
-    case PA_F16: prefill_share_merge_kernel<F16><<<grid, block, 0, stream>>>(a, rows, head_dim); break;
-    case PA_F32: prefill_share_merge_kernel<F32><<<grid, block, 0, stream>>>(a, rows, head_dim); break;
+    case PA_BF16: PA_PF_MERGE(Bf16) break;
+    case PA_F16: PA_PF_MERGE(F16) break;
+    case PA_F32: PA_PF_MERGE(F32) break;
     default: return hipErrorInvalidValue;
   }
+#undef PA_PF_MERGE
   return hipGetLastError();
 }
 
