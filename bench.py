@@ -501,7 +501,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--path", choices=["decode", "balanced", "fused", "splitk"],
-                    default="balanced")
+                    default="fused")
     ap.add_argument("--split-tokens", type=int, default=512)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=10.0)

@@ -264,9 +264,6 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
       const int64_t src = ((int64_t)r * hkv + kvh) * D;
       O::load_new(nr, static_cast<const S*>(a.k_new) + src, static_cast<const S*>(a.v_new) + src,
                   lane, a.k_scale, a.v_scale);
-      const int64_t dst = slot * view.rs + (int64_t)kvh * D;
-      O::store_new(nr, static_cast<KS*>(const_cast<void*>(a.k_cache)) + dst,
-                   static_cast<KS*>(const_cast<void*>(a.v_cache)) + dst, lane);
     }
     const int new_row = (seq_len - 1) & (kBlockTokens - 1), new_blk = nb - 1 - b;
     auto patch = [&](typename O::KV& kv, int i) {
@@ -277,6 +274,14 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     // every wave of the workgroup walks the same blocks: same trip count
     stream_blocks<E, D, bal_depth<E>(), PA_BAL_SYNC != 0>(st, qop, view, b, len, key_end,
                                                          seq_len, a.scale_log2, lane, patch);
+    if (subst) {
+      // stored after the walk, so the new rows' loads are not waited for
+      // before the first block; this piece is the only reader of the slot
+      // and used the rows from registers
+      const int64_t dst = slot * view.rs + (int64_t)kvh * D;
+      O::store_new(nr, static_cast<KS*>(const_cast<void*>(a.k_cache)) + dst,
+                   static_cast<KS*>(const_cast<void*>(a.v_cache)) + dst, lane);
+    }
     st.l = sum_xor16(st.l);
     st.l = sum_xor32(st.l);
 
