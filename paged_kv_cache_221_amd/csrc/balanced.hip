@@ -325,93 +325,94 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
   }
 }
 
-// One wave per (request, query head, query token): renormalises the pieces of a segment
-// that was cut between workgroups. The record gives where the pieces are;
-// then every piece's LSE (lane j reads piece j) and the outputs of the first
-// kMergeBatch pieces (lanes over head_dim) are loaded together, so a segment
-// of up to kMergeBatch pieces costs two dependent memory round trips; later
-// pieces are loaded kMergeBatch at a time.
+// Stores 8 consecutive output values in the storage dtype.
+template <class E, int D>
+__device__ inline void store8(typename Ops<E, D>::storage* dst, const float* v) {
+  using S = typename Ops<E, D>::storage;
+  if constexpr (sizeof(S) == 2) {
+    unsigned w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (unsigned)Ops<E, D>::to_storage(v[2 * j]) |
+             ((unsigned)Ops<E, D>::to_storage(v[2 * j + 1]) << 16);
+    *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+// One wave per (request, KV head): renormalises the pieces of a segment that
+// was cut between workgroups [P1 §07: out = sum_j w_j o_j / sum_j w_j,
+// w_j = exp(lse_j - max lse), here in log2 units]. The record gives the first
+// piece slot and the piece count; each slot holds slot_rows x D floats, of
+// which the request's n * group rows are valid. Lanes take 8 consecutive
+// values of the flattened valid rows and fold kMergeBatch pieces per memory
+// round trip with a running maximum, so a segment of up to kMergeBatch
+// pieces costs two dependent round trips (record, then pieces).
 constexpr int kMergeBatch = 16;
-template <class E>
+template <class E, int D>
 __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const BalancedArgs a) {
+  using S = typename Ops<E, D>::storage;
   const int lane = threadIdx.x & (kWave - 1);
-  const int toks = a.slot_rows / a.group;  // query tokens a slot holds
   const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  if (unit >= (int64_t)a.num_seqs * a.num_heads * toks) return;
-  const int tok = (int)(unit % toks);
-  const int64_t rh = unit / toks;
-  const int r = (int)(rh / a.num_heads);
-  const int h = (int)(rh - (int64_t)r * a.num_heads);
-  const int g = a.group, kvh = h / g;
+  if (unit >= (int64_t)a.num_seqs * a.num_kv_heads) return;
+  const int r = (int)(unit / a.num_kv_heads);
+  const int kvh = (int)(unit - (int64_t)r * a.num_kv_heads);
+  const int g = a.group;
   int q_lo, n_r;
   request_rows(a, r, &q_lo, &n_r);
-  if (!single_tile(n_r, g) || tok >= n_r) return;
-  const int D = a.head_dim;
-  const int2 rec = a.records[(int64_t)r * a.num_kv_heads + kvh];
+  if (!single_tile(n_r, g)) return;
+  const int2 rec = a.records[unit];
   const int np = rec.y;
   if (np <= 0) return;  // written whole by one workgroup, or an empty request
-  const int d0 = lane, d1 = lane + kWave;
   const int64_t sr = a.slot_rows;
-  const int srow = tok * g + (h - kvh * g);  // row within the slot
-  const float* lse = a.part_lse + (int64_t)rec.x * sr + srow;
-  const float* po = a.part_o + ((int64_t)rec.x * sr + srow) * D;
-  // issue the first batch of outputs together with the LSEs
-  float o0[kMergeBatch], o1[kMergeBatch];
+  const float* po = a.part_o + (int64_t)rec.x * sr * D;
+  const float* pl = a.part_lse + (int64_t)rec.x * sr;
+  for (int f = lane * 8; f < n_r * g * D; f += kWave * 8) {
+    const int row = f / D, dim = f - row * D;
+    float m = neg_inf(), wsum = 0.f, acc[8];
 #pragma unroll
-  for (int k = 0; k < kMergeBatch; ++k) {
-    const bool ok = k < np;
-    o0[k] = ok && d0 < D ? po[(int64_t)k * sr * D + d0] : 0.f;
-    o1[k] = ok && d1 < D ? po[(int64_t)k * sr * D + d1] : 0.f;
-  }
-  float mx = neg_inf();
-  for (int j = lane; j < np; j += kWave) mx = fmaxf(mx, lse[(int64_t)j * sr]);
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int k0 = 0; k0 < np; k0 += kMergeBatch) {
+      float l[kMergeBatch];
+      f32x4 v[kMergeBatch][2];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, xor_shuffle(mx, m));
-  const float mu = mx == neg_inf() ? 0.f : mx;
-  float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
-  for (int c = 0; c < np; c += kWave) {
-    const int j = c + lane;
-    const float w = j < np ? fast_exp2(lse[(int64_t)j * sr] - mu) : 0.f;
-    wsum += w;
-    const int cnt = min(kWave, np - c);
-    // pieces c + b0 .. c + b0 + kMergeBatch - 1: all loads first, then the sums
-    for (int b0 = 0; b0 < cnt; b0 += kMergeBatch) {
-      float x0[kMergeBatch], x1[kMergeBatch];
-      if (c == 0 && b0 == 0) {
+      for (int kk = 0; kk < kMergeBatch; ++kk) {
+        // past the last piece: reload it (in bounds), weighted 0 below
+        const int64_t k = min(k0 + kk, np - 1);
+        l[kk] = pl[k * sr + row];
+        const f32x4* src = reinterpret_cast<const f32x4*>(po + k * sr * D + f);
+        v[kk][0] = src[0];
+        v[kk][1] = src[1];
+      }
+      float mb = m;
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
-          x0[k] = o0[k];
-          x1[k] = o1[k];
-        }
-      } else {
+      for (int kk = 0; kk < kMergeBatch; ++kk)
+        if (k0 + kk < np) mb = fmaxf(mb, l[kk]);
+      const float mu = mb == neg_inf() ? 0.f : mb;
+      const float alpha = fast_exp2(m - mu);  // 0 while nothing was folded (m = -inf)
+      wsum *= alpha;
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
-          const bool ok = b0 + k < cnt;
-          const float* src = po + (int64_t)(c + b0 + k) * sr * D;
-          x0[k] = ok && d0 < D ? src[d0] : 0.f;
-          x1[k] = ok && d1 < D ? src[d1] : 0.f;
+      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+      for (int kk = 0; kk < kMergeBatch; ++kk) {
+        const float w = k0 + kk < np ? fast_exp2(l[kk] - mu) : 0.f;
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += w * v[kk][0][e];
+          acc[4 + e] += w * v[kk][1][e];
         }
       }
-#pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        // b0 + k < kWave: b0 is a multiple of kMergeBatch below cnt <= kWave
-        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), b0 + k));
-        acc0 += wk * x0[k];  // zero past cnt (loaded as 0, weight 0)
-        acc1 += wk * x1[k];
-      }
+      m = mb;
     }
-  }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) wsum += xor_shuffle(wsum, m);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  using S = typename E::storage;
-  S* out = static_cast<S*>(a.out) + (((int64_t)q_lo + tok) * a.num_heads + h) * D;
-  if constexpr (sizeof(S) == 2) {
-    if (d0 < D) out[d0] = E::from_float(acc0 * inv);
-    if (d1 < D) out[d1] = E::from_float(acc1 * inv);
-  } else {
-    if (d0 < D) out[d0] = acc0 * inv;
-    if (d1 < D) out[d1] = acc1 * inv;
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    const int tok = row / g, hh = row - tok * g;
+    S* dst = static_cast<S*>(a.out) + (((int64_t)q_lo + tok) * a.num_heads + kvh * g + hh) * D + dim;
+    store8<E, D>(dst, acc);
   }
 }
 
@@ -421,8 +422,8 @@ hipError_t launch_bal(const BalancedArgs& a, hipStream_t stream) {
       <<<dim3((unsigned)(a.total_waves / NW)), dim3(NW * kWave), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t units = (int64_t)a.num_seqs * a.num_heads * (a.slot_rows / a.group);
-  balanced_merge_kernel<E><<<dim3((unsigned)((units + 3) / 4)), dim3(4 * kWave), 0, stream>>>(a);
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
+  balanced_merge_kernel<E, D><<<dim3((unsigned)((units + 3) / 4)), dim3(4 * kWave), 0, stream>>>(a);
   return hipGetLastError();
 }
 
