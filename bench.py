@@ -257,8 +257,8 @@ def cpu_baseline(st, layout, budget_s: float):
 
 SECONDARY_LEGS = ("long-context-splitk-bf16", "llama2-7b-mha-decode-fp16", "mixed-step-bf16",
                   "mixed-step-prefill-chunks-bf16", "llama3-8b-decode-e4m3-cache",
-                  "rope-write-kv-mixed-step-bf16", "copy-on-write-blocks-bf16",
-                  "block-manager-host")
+                  "llama3-8b-spec-verify-q4-bf16", "rope-write-kv-mixed-step-bf16",
+                  "copy-on-write-blocks-bf16", "block-manager-host")
 
 
 def secondary(args, only=None):
@@ -314,6 +314,7 @@ def secondary(args, only=None):
         torch.cuda.empty_cache()
     for name, leg in (("mixed-step-prefill-chunks-bf16", bench_prefill_only),
                       ("llama3-8b-decode-e4m3-cache", bench_fp8_decode),
+                      ("llama3-8b-spec-verify-q4-bf16", bench_spec_verify),
                       ("rope-write-kv-mixed-step-bf16", bench_rope_write),
                       ("copy-on-write-blocks-bf16", bench_copy_blocks)):
         if only is None or name == only:
@@ -382,6 +383,50 @@ def bench_fp8_decode(k: int, copies: int = 4):
             "attention_frac_of_8TBps": round(nbytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": nbytes,
             "decode_tokens_per_s_per_layer": round(lay.num_seqs / (kern * 1e-3), 1)}
+
+
+def bench_spec_verify(k: int, copies: int = 4):
+    """The Llama-3-8B decode batch (same lengths and KV bytes) with every
+    request verifying 4 tokens at once, as speculative decoding does: the
+    step writes the 256 new tokens' K/V, then pa_varlen with a workspace (GQA
+    group 4 x 4 tokens = one 16-row tile, the balanced kernel). Input copies
+    rotate as in the decode bench. Algorithmic bytes: per-request KV, q and
+    out, tables; FLOPs: exact causal pairs."""
+    import torch
+    import paged_kv_cache_221_amd as pa
+    from workloads import llama3_8b_spec_verify
+    from workloads.tensors import materialize
+    lay = llama3_8b_spec_verify()
+    sts = [materialize(lay, "cuda", poison=False, seed_offset=i) for i in range(copies)]
+    ws = torch.zeros(pa.pa_varlen_workspace_bytes(sts[0].k_cache, sts[0].v_cache, lay.num_seqs,
+                                                  sts[0].q.shape[0], lay.num_heads,
+                                                  sts[0].block_table.shape[1]),
+                     dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(st.q) for st in sts]
+
+    def make(st, out):
+        def step(ev=None):
+            pa.pa_write_kv(st.k_cache, st.v_cache, st.k_new, st.v_new, st.slot_mapping)
+            if ev is not None:
+                ev[0].record()
+            pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                         st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
+                         out=out, workspace=ws)
+            if ev is not None:
+                ev[1].record()
+        return step
+    ms, kern = time_steps([make(st, o) for st, o in zip(sts, outs)], max(k, 10), 3, True)
+    nbytes, flops = varlen_bytes(lay), causal_flops(lay)
+    tokens = int(lay.query_lens.sum())
+    print(f"[bench] spec verify q4: attention {kern:.4f} ms", file=sys.stderr, flush=True)
+    del sts, outs, ws
+    torch.cuda.empty_cache()
+    return {"query_len": 4, "step_ms": round(ms, 4), "attention_kernel_ms": round(kern, 4),
+            "attention_GBps": round(nbytes / (kern * 1e-3) / 1e9, 1),
+            "attention_frac_of_8TBps": round(nbytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes, "flops": flops,
+            "TFLOPs": round(flops / (kern * 1e-3) / 1e12, 1),
+            "verified_tokens_per_s_per_layer": round(tokens / (kern * 1e-3), 1)}
 
 
 def bench_rope_write(k: int):

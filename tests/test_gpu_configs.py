@@ -1,4 +1,5 @@
-"""GPU parity at the five workloads' full sizes.
+"""GPU parity at the five workloads' full sizes, and at the Llama-3-8B decode
+batch's size for speculative verification (several query tokens per request).
 
 Every cache write is checked bit for bit on the blocks the sampled requests
 and the new tokens touch, and the rest of the pool is checked unchanged on the
@@ -14,8 +15,8 @@ import torch
 
 import oracle
 import paged_kv_cache_221_amd as pa
-from workloads import (llama2_7b_mha_decode, llama3_8b_decode, long_context_splitk,
-                       mixed_step, tiny_decode_fp32)
+from workloads import (llama2_7b_mha_decode, llama3_8b_decode, llama3_8b_spec_verify,
+                       long_context_splitk, mixed_step, tiny_decode_fp32)
 from workloads.tensors import materialize
 
 from _parity import (TOL, Snapshot, check_cache_after_write, gpu_rows, gpu_write, max_err,
@@ -153,6 +154,28 @@ def test_mixed_step_sampled(shuffled):
     others = [r for r in range(lay.num_seqs) if r not in prefill and r not in sharers]
     req = sorted(set(prefill) | set(sharers[:3]) | set(rng.choice(others, 6, replace=False).tolist())
                  | {int(np.argmax(lay.seq_lens))})
+    snap = _write_and_check(st, req)
+    out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    want, _ = oracle.paged_varlen(snap.q, snap.k, snap.v, lay.cu_seqlens_q, lay.seq_lens,
+                                  lay.block_table, lay.scale, lay.block_size, lay.dtype,
+                                  requests=req)
+    rows = rows_of(lay, req)
+    err = max_err(gpu_rows(out, lay.dtype)[rows], want[rows])
+    print(f"{lay.name}: {len(req)} requests / {len(rows)} rows, max|err| = {err:.3e}",
+          flush=True)
+    assert err <= TOL[lay.dtype]
+
+
+@pytest.mark.parametrize("query_len", [4, 8])
+def test_llama3_8b_spec_verify_sampled(query_len):
+    """The Llama-3-8B decode batch verifying 4 tokens per request (GQA group
+    4: exactly one 16-row tile, the balanced kernel) or 8 (two tiles: the
+    prefill kernel), on a seeded sample of requests with the longest."""
+    lay = llama3_8b_spec_verify(query_len=query_len)
+    st = materialize(lay, "cuda")
+    req = _sample(lay, 12, 66 + query_len)
     snap = _write_and_check(st, req)
     out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
                        st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale)

@@ -274,6 +274,37 @@ def test_varlen_balanced_workspace_contents_do_not_matter(gpu_lib):
         pa.pa_varlen(*args, workspace=ws[:need - 1])
 
 
+# (num_heads, num_kv_heads, query lengths): for each GQA group the lengths
+# just below, at and above one 16-row tile (query_len x group = 16)
+SPEC_CASES = [(8, 8, (15, 16, 17, 2)), (8, 4, (7, 8, 9, 3)), (16, 4, (3, 4, 5, 8)),
+              (16, 2, (1, 2, 3, 4))]
+
+
+@pytest.mark.parametrize("path", ["balanced", "direct"])
+@pytest.mark.parametrize("case", SPEC_CASES, ids=lambda c: f"{c[0]}-{c[1]}")
+def test_multi_token_decode_parity(gpu_lib, case, path):
+    """Speculative-verify shapes [P3 §5.2]: requests checking several tokens
+    at once, causal among themselves, beside one-token decode rows. Lengths
+    whose rows fit one 16-row tile run in the decode kernels with the
+    bottom-right mask inside the tile; one more token moves the request to
+    the prefill kernel. Contexts end mid-block and on block edges."""
+    hq, hkv, qlens = case
+    ctxs = (37, 64, 250, 16)
+    lay = small_varlen(880 + hq + hkv, dtype="bf16", num_heads=hq, num_kv_heads=hkv,
+                       prefill=tuple(zip(qlens, ctxs)), decode_lens=(1, 90, 700))
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
+                       workspace="auto" if path == "balanced" else None)
+    torch.cuda.synchronize()
+    want, _ = varlen_oracle(st, snap, req)
+    err = max_err(gpu_rows(out, "bf16"), want)
+    print(f"{lay.name} {hq}/{hkv} q={qlens} {path}: max|err| = {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
 def test_varlen_all_decode_matches_decode_oracle(gpu_lib):
     lay = small_decode(30, dtype="bf16", batch=9, min_len=1, max_len=600)
     st, snap, req = prepare(lay)

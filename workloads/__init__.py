@@ -9,6 +9,7 @@ from .configs import (  # noqa: F401
     BENCH_CONFIGS,
     tiny_decode_fp32,
     llama3_8b_decode,
+    llama3_8b_spec_verify,
     long_context_splitk,
     llama2_7b_mha_decode,
     mixed_step,

@@ -85,6 +85,19 @@ def mixed_step_prefill_only(seed: int = 5) -> StepLayout:
                         value_std=0.5)
 
 
+def llama3_8b_spec_verify(seed: int = 2, batch: int = 64, query_len: int = 4) -> StepLayout:
+    """The Llama-3-8B-shaped decode batch (the same lengths, U{512..4096})
+    with every request checking ``query_len`` tokens in one step, the verify
+    step of speculative decoding [P3 §5.2]: the drafted tokens attend
+    causally to the context and to each other. bf16, pool 1.2x need."""
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    lens = rng.integers(512, 4096, size=batch, endpoint=True)
+    return build_layout(f"llama3-8b-spec-verify-q{query_len}-bf16", "bf16", lens,
+                        [query_len] * batch, num_heads=32, num_kv_heads=8, head_dim=128,
+                        block_size=16, seed=seed, pool_factor=1.2,
+                        max_blocks_per_seq=4096 // 16, value_std=0.5)
+
+
 BENCH_CONFIGS = {
     "tiny-decode-fp32": tiny_decode_fp32,
     "llama3-8b-decode-bf16": llama3_8b_decode,
