@@ -51,6 +51,15 @@ namespace {
 #ifndef PA_BAL_SYNC
 #define PA_BAL_SYNC 1
 #endif
+// Work items charged to each (request, head group) segment beyond its
+// blocks: a piece's fixed cost (its query load, the refill of the block
+// pipeline before its first block arrives, the final reduction and stores),
+// so that a share crossing more segment boundaries gets fewer blocks. On the
+// 64-request Llama-3-8B batch 3 and 4 were best (0: +2 us per call, 6: +2 us).
+#ifndef PA_BAL_PIECE_COST
+#define PA_BAL_PIECE_COST 3
+#endif
+constexpr int kPieceCost = PA_BAL_PIECE_COST;
 template <class E>
 constexpr int bal_depth() {
   return sizeof(typename E::kv_storage) == 4   ? (PA_BAL_DEPTH + 1) / 2
@@ -160,7 +169,8 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
   const int B = a.num_seqs;
   const int max_len = a.max_blocks * kBlockTokens;
 
-  // 1. prefix sums of per-request block counts, in LDS
+  // 1. prefix sums of per-request item counts (blocks plus the fixed cost of
+  //    a segment, per head group), in LDS
   constexpr int T = NW * kWave;
   const int per = (B + T - 1) / T;
   const int c0 = min(tid * per, B), c1 = min(c0 + per, B);
@@ -170,12 +180,13 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     request_rows(a, i, &q_lo, &n);
     const int len = min(max(a.seq_lens[i], 0), max_len);
     const int nb = single_tile(n, a.group) ? (len + kBlockTokens - 1) / kBlockTokens : 0;
-    s_prefix[i + 1] = nb;
-    chunk += nb;
+    const int items = nb > 0 ? nb + kPieceCost : 0;
+    s_prefix[i + 1] = items;
+    chunk += items;
   }
-  int total_blocks = 0;
-  int run = block_exclusive_sum<NW>(chunk, s_tmp, &total_blocks);
-  total_blocks = __builtin_amdgcn_readfirstlane(total_blocks);
+  int total_items = 0;
+  int run = block_exclusive_sum<NW>(chunk, s_tmp, &total_items);
+  total_items = __builtin_amdgcn_readfirstlane(total_items);
   for (int i = c0; i < c1; ++i) {
     run += s_prefix[i + 1];
     s_prefix[i + 1] = run;
@@ -197,11 +208,12 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     }
   }
 
-  // 2. this workgroup's share of the W = HG * total_blocks items
+  // 2. this workgroup's share of the W = HG * total_items items; a segment's
+  //    first kPieceCost items stand for its fixed cost and hold no block
   const int hkv = a.num_kv_heads, g = a.group;
   const int HG = hkv / NW;  // head groups
   const int64_t TWG = a.total_waves / NW;
-  const Shares sh{(int64_t)HG * total_blocks, TWG};
+  const Shares sh{(int64_t)HG * total_items, TWG};
   const int64_t head_slots = TWG + (int64_t)B * HG;  // slots per head (wave)
   const int64_t t = blockIdx.x;
   const int64_t lo = sh.begin(t), hi = sh.begin(t + 1), j = sh.range(t);
@@ -225,10 +237,16 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     while (r < B - 1 && (int64_t)HG * prefix(r + 1) <= x) ++r;
     r = __builtin_amdgcn_readfirstlane(r);
     const int p_r = prefix(r);
-    const int nb = prefix(r + 1) - p_r;
+    const int seg = prefix(r + 1) - p_r;  // items per head group of request r
+    const int nb = seg - kPieceCost;      // its blocks
     const int off = __builtin_amdgcn_readfirstlane((int)(x - (int64_t)HG * p_r));
-    const int hg = __builtin_amdgcn_readfirstlane(off / nb);
-    const int b = __builtin_amdgcn_readfirstlane(off - hg * nb);
+    const int hg = __builtin_amdgcn_readfirstlane(off / seg);
+    const int item = __builtin_amdgcn_readfirstlane(off - hg * seg);
+    if (item < kPieceCost) {  // the segment's fixed-cost items: no block
+      x += min((int64_t)(kPieceCost - item), hi - x);
+      continue;
+    }
+    const int b = item - kPieceCost;
     const int len = __builtin_amdgcn_readfirstlane((int)min((int64_t)(nb - b), hi - x));
     const int seq_len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[r], 0), max_len));
     int q_lo, n_r;
@@ -315,7 +333,7 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
       // every piece of a segment writes the same record; a whole one writes 0
       int2 rec{0, 0};
       if (!whole) {
-        const int64_t s0 = (int64_t)HG * p_r + (int64_t)hg * nb;
+        const int64_t s0 = (int64_t)HG * p_r + (int64_t)hg * seg + kPieceCost;  // block 0's item
         const int64_t first = (int64_t)wave * head_slots + piece_slot(sh.range_of(s0), sg);
         rec = int2{(int)first, (int)(sh.range_of(s0 + nb - 1) - sh.range_of(s0) + 1)};
       }
