@@ -39,10 +39,12 @@
 #define PA_PREFILL_OCC 2
 #endif
 // Fixed cost of a tile in the equal-share prefill, in KV blocks: a piece
-// pays its query loads, pipeline fill and stores, so shares of many short
-// tiles get fewer blocks.
+// pays its query loads, pipeline fill and stores (a cut tile's fp32 partial
+// rows are 64 KB, the bytes of eight of its KV block slices), so shares of
+// many short tiles get fewer blocks. On the mixed step's four chunks: 0 ->
+// 190 us, 2 -> 177, 4 -> 166, 8 -> 150, 12-16 -> 148-151, 32 -> 157.
 #ifndef PA_PREFILL_TILE_COST
-#define PA_PREFILL_TILE_COST 2
+#define PA_PREFILL_TILE_COST 8
 #endif
 
 namespace pa {
