@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import paged_kv_cache_221_amd as pa
-from workloads import small_decode, small_varlen, tiny_decode_fp32
+from workloads import build_layout, small_decode, small_varlen, tiny_decode_fp32
 from workloads.tensors import materialize, raw_bits
 
 from _parity import (TOL, check_cache_after_write, decode_oracle, gpu_rows, gpu_write,
@@ -149,6 +149,37 @@ def test_balanced_decode_parity(gpu_lib, case):
     err = max_err(gpu_rows(out, dtype), want)
     print(f"{lay.name}: balanced max|err| = {err:.3e}", flush=True)
     assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 16, 4, 64),
+                                            ("f32", 8, 2, 128)])
+def test_balanced_decode_many_short_requests(gpu_lib, dtype, hq, hkv, d):
+    """Hundreds of one- and two-block requests beside a few long ones: each
+    segment also counts fixed-cost items that hold no block, so shares of a
+    few items start, end or lie wholly inside them; a share with no block
+    writes nothing, and every piece still lands in its own slot."""
+    rng = np.random.Generator(np.random.PCG64(hq + hkv + d))
+    lens = ([1] * 150 + [16] * 60 + [17] * 40 + [2] * 80 + [33] * 60 + [1500, 2100, 700])
+    lens = rng.permutation(np.asarray(lens)).tolist()
+    lay = build_layout(f"many-short-{dtype}", dtype, lens, [1] * len(lens), num_heads=hq,
+                       num_kv_heads=hkv, head_dim=d, block_size=16, seed=hq + d,
+                       pool_factor=1.2)
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    for path in ("balanced", "fused"):
+        if path == "balanced":
+            out = pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table,
+                                        st.seq_lens, lay.max_seq_len, lay.scale)
+        else:
+            out = pa.pa_write_decode_balanced(st.k_cache, st.v_cache, st.q, st.k_new,
+                                              st.v_new, st.slot_mapping, st.block_table,
+                                              st.seq_lens, lay.max_seq_len, lay.scale)
+        torch.cuda.synchronize()
+        want, _ = decode_oracle(st, snap, req)
+        err = max_err(gpu_rows(out, dtype), want)
+        print(f"{lay.name} {path}: {len(lens)} requests, max|err| = {err:.3e}", flush=True)
+        assert err <= TOL[dtype]
 
 
 def test_balanced_decode_empty_requests_and_reuse(gpu_lib):
