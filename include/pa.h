@@ -37,7 +37,9 @@
  *   is broken: an out-of-pool slot is not written, an out-of-pool block id is
  *   read as zeros (no memory access), lengths are clipped to
  *   max_blocks_per_seq * bs.
- *   Results for such inputs are unspecified.
+ *   Results for such inputs are unspecified. The Python package's
+ *   validate_metadata() checks the whole contract on the host (a debug aid:
+ *   it copies the arrays from the device).
  * - Supported now: block_size 16; head_dim 64 or 128; Hq % Hkv == 0 with
  *   Hq / Hkv <= 16; fp32, fp16 and bf16 storage with fp32 accumulation, and
  *   E4M3 KV caches (bf16 arithmetic on the exactly widened codes) in

@@ -24,3 +24,4 @@ from .api import (  # noqa: F401
     pa_write_decode_balanced,
     pa_write_kv,
 )
+from .validate import PaMetadataError, validate_metadata  # noqa: F401
