@@ -465,21 +465,32 @@ def bench_rope_write(k: int):
     ang = torch.rand((maxpos, 64), generator=gen, device="cuda") * 100
     cos_sin = torch.cat([ang.cos(), ang.sin()], dim=1).contiguous()
     positions = (torch.arange(t, device="cuda", dtype=torch.int32) % maxpos).contiguous()
-    q = st.q.clone()
+    # 12 copies of the new tokens' q, K and V (~320 MB) rotate, so no call
+    # finds its inputs in the 256 MB last-level cache; one pair of events
+    # around a run of calls, as a single ~10 us call would be mostly event
+    # overhead
+    copies = [(st.q.clone(), st.k_new.clone(), st.v_new.clone()) for _ in range(12)]
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        pa.pa_rope_write_kv(st.k_cache, st.v_cache, q, st.k_new, st.v_new, st.slot_mapping,
-                            positions, cos_sin, 128, True)
-        if ev is not None:
-            ev[1].record()
-    _, kern = time_steps([step], max(k, 10), 3, True)
+    def call(i):
+        q, kn, vn = copies[i % len(copies)]
+        pa.pa_rope_write_kv(st.k_cache, st.v_cache, q, kn, vn, st.slot_mapping, positions,
+                            cos_sin, 128, True)
+    for i in range(len(copies)):
+        call(i)
+    torch.cuda.synchronize()
+    n = 4 * len(copies)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    kern = e0.elapsed_time(e1) / n
     e = 2
     nbytes = t * (2 * lay.num_heads * lay.head_dim * e + 4 * lay.num_kv_heads * lay.head_dim * e
                   + 4 + 8 + 128 * 4)
     print(f"[bench] rope + write: {kern:.4f} ms", file=sys.stderr, flush=True)
-    del st, q
+    del st, copies
     torch.cuda.empty_cache()
     return {"tokens": t, "kernel_ms": round(kern, 4),
             "GBps": round(nbytes / (kern * 1e-3) / 1e9, 1),
