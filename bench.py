@@ -272,9 +272,17 @@ def secondary_isolated(args):
     for leg in SECONDARY_LEGS:
         cmd = [sys.executable, os.path.abspath(__file__), "--only", leg,
                "--steps", str(args.steps), "--warmup", str(args.warmup)]
-        p = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
-        if p.returncode != 0:
-            raise RuntimeError(f"secondary leg {leg} failed with status {p.returncode}")
+        try:
+            p = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+        except subprocess.TimeoutExpired:
+            res[leg] = {"error": "timed out after 900 s"}
+            continue
+        if p.returncode != 0 or not p.stdout.strip():
+            # a failed leg is reported, and the headline line still printed
+            print(f"[bench] secondary leg {leg} failed with status {p.returncode}",
+                  file=sys.stderr, flush=True)
+            res[leg] = {"error": f"exit status {p.returncode}"}
+            continue
         res.update(json.loads(p.stdout.strip().splitlines()[-1])["secondary"])
     return res
 
