@@ -190,13 +190,14 @@ __device__ inline unsigned bf16x4_to_fp8(unsigned lo, unsigned hi, float scale) 
 }
 
 // Four E4M3 codes (byte k of w is element k) -> four bf16, as two packed
-// words in the same order.
+// words in the same order. gfx950 converts two codes to two bf16 in one
+// instruction; with a scale of 1 that is exact, since every E4M3 value
+// (subnormals, signed zeros) is a bf16 value and NaN stays NaN (checked on the
+// GPU for all 256 codes). It halves the widening work against converting to
+// fp32 and packing to bf16.
 __device__ inline void fp8x4_to_bf16(unsigned w, unsigned* lo, unsigned* hi) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  *lo = Bf16::pack2(a.x, a.y);
-  *hi = Bf16::pack2(b.x, b.y);
+  *lo = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  *hi = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
 // --------------------------------------------------- operand load / compute

@@ -179,3 +179,41 @@ def test_fp8_copy_blocks_bit_exact(gpu_lib):
     want_k, want_v = copy_blocks(s.k, s.v, [tuple(p) for p in pairs.tolist()])
     assert np.array_equal(raw_bits(st.k_cache, "e4m3"), want_k)
     assert np.array_equal(raw_bits(st.v_cache, "e4m3"), want_v)
+
+
+@pytest.mark.parametrize("path", ["decode", "balanced", "splitk"])
+def test_e4m3_single_key_widens_every_code_exactly(gpu_lib, path):
+    """With one key its softmax weight is exactly 1, so each output element is
+    its V code's value (scales 1): every E4M3 value is a bf16 value, so the
+    bf16 output must hold it exactly, and a NaN code must give NaN. The key's
+    V row holds all 256 codes four times over the 8 KV heads. (A -0 code comes
+    out +0: the block's masked keys add +0 terms.)"""
+    hkv, hq, d, bs = 8, 32, 128, 16
+    codes = np.tile(np.arange(256, dtype=np.uint8), 4)
+    k = torch.zeros((2, bs, hkv, d), dtype=torch.uint8, device="cuda")
+    v = torch.zeros_like(k)
+    k[1, 0] = 0x38                      # 1.0
+    v[1, 0] = torch.from_numpy(codes.reshape(hkv, d)).cuda()
+    kc, vc = k.view(torch.float8_e4m3fn), v.view(torch.float8_e4m3fn)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(61)
+    q = torch.randn((1, hq, d), generator=gen, device="cuda").to(torch.bfloat16)
+    bt = torch.tensor([[1]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([1], dtype=torch.int32, device="cuda")
+    scale = d ** -0.5
+    kw = dict(k_scale=1.0, v_scale=1.0)
+    if path == "decode":
+        out = pa.pa_decode(kc, vc, q, bt, lens, 1, scale, **kw)
+    elif path == "balanced":
+        out = pa.pa_decode_balanced(kc, vc, q, bt, lens, 1, scale, **kw)
+    else:
+        o, l = pa.pa_decode_splitk(kc, vc, q, bt, lens, 1, 16, scale, **kw)
+        out = pa.pa_lse_merge(o, l, lens, 1, 16, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()[0]
+    want = fp8.decode(codes).reshape(hkv, d)
+    for h in range(hq):
+        w = want[h // (hq // hkv)]
+        nan = np.isnan(w)
+        assert np.array_equal(np.isnan(got[h]), nan), f"head {h}: NaN codes"
+        assert np.array_equal(got[h][~nan], w[~nan]), f"head {h}: a code widened inexactly"
