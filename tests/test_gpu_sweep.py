@@ -1,0 +1,84 @@
+"""Seeded random sweep of the balanced kernels against the oracle.
+
+The balanced decode cuts the batch's (request, head group, block) items, plus
+a fixed cost per segment, into one equal share per resident workgroup, so
+where shares start and end depends on every length in the batch. Each case
+draws a batch size, ragged lengths with a few long outliers, a GQA shape and
+a dtype from a seed, and checks the balanced decode, the fused write + decode
+step and a varlen step of short multi-token queries and decode rows against
+the fp64 oracle (errors within the usual bounds).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_221_amd as pa
+from workloads import build_layout
+
+from _parity import (TOL, decode_oracle, gpu_rows, gpu_write, max_err, prepare,
+                     varlen_oracle)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(32, 8, 128), (16, 4, 64), (8, 2, 128), (16, 16, 128), (8, 1, 64), (64, 8, 128)]
+
+
+def _draw(seed):
+    rng = np.random.Generator(np.random.PCG64(7000 + seed))
+    hq, hkv, d = SHAPES[seed % len(SHAPES)]
+    dtype = ("bf16", "f16", "f32")[seed % 3]
+    b = int(rng.choice([1, 2, 5, 17, 60, 130, 257]))
+    lens = rng.integers(1, 400, size=b)
+    spikes = rng.random(b) < 0.08
+    lens[spikes] = rng.integers(1500, 4000, size=int(spikes.sum()))
+    return rng, hq, hkv, d, dtype, lens.tolist()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_balanced_and_fused_decode_sweep(gpu_lib, seed):
+    rng, hq, hkv, d, dtype, lens = _draw(seed)
+    lay = build_layout(f"sweep-{seed}", dtype, lens, [1] * len(lens), num_heads=hq,
+                       num_kv_heads=hkv, head_dim=d, block_size=16, seed=seed,
+                       pool_factor=1.3)
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    want, _ = decode_oracle(st, snap, req)
+    bal = pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                                lay.max_seq_len, lay.scale)
+    fused = pa.pa_write_decode_balanced(st.k_cache, st.v_cache, st.q, st.k_new, st.v_new,
+                                        st.slot_mapping, st.block_table, st.seq_lens,
+                                        lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    e1 = max_err(gpu_rows(bal, dtype), want)
+    e2 = max_err(gpu_rows(fused, dtype), want)
+    print(f"seed {seed}: {len(lens)} requests {hq}/{hkv}/{d} {dtype}: balanced {e1:.2e} "
+          f"fused {e2:.2e}", flush=True)
+    assert e1 <= TOL[dtype] and e2 <= TOL[dtype]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_varlen_short_queries_sweep(gpu_lib, seed):
+    rng, hq, hkv, d, dtype, lens = _draw(100 + seed)
+    g = hq // hkv
+    # query lengths that fit one 16-row tile (balanced kernel), a few longer
+    # ones (prefill kernel), never more than the request's keys
+    qmax = max(1, 16 // g)
+    qlens = [int(min(L, rng.integers(1, qmax + 1))) for L in lens]
+    for i in rng.choice(len(lens), size=min(2, len(lens)), replace=False):
+        qlens[i] = int(min(lens[i], qmax + 1 + rng.integers(0, 20)))
+    lay = build_layout(f"sweep-varlen-{seed}", dtype, lens, qlens, num_heads=hq,
+                       num_kv_heads=hkv, head_dim=d, block_size=16, seed=100 + seed,
+                       pool_factor=1.3)
+    st, snap, req = prepare(lay)
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale)
+    torch.cuda.synchronize()
+    want, _ = varlen_oracle(st, snap, req)
+    err = max_err(gpu_rows(out, dtype), want)
+    print(f"seed {seed}: {len(lens)} requests, queries up to {max(qlens)}, {hq}/{hkv}/{d} "
+          f"{dtype}: max|err| = {err:.2e}", flush=True)
+    assert err <= TOL[dtype]
