@@ -547,13 +547,25 @@ __global__ __launch_bounds__(4 * kWave) void prefill_share_merge_kernel(const At
   using S = typename E::storage;
   const int token = (int)(unit / a.num_kv_heads), kvh = (int)(unit - (int64_t)token * a.num_kv_heads);
   S* out = static_cast<S*>(a.out) + ((int64_t)token * a.num_heads + kvh * g + hh) * D + d0;
+  // the lane's DPL consecutive outputs in 8- or 16-byte stores
+  if constexpr (sizeof(S) == 2) {
+    unsigned w[DPL / 2];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) {
-    if constexpr (sizeof(S) == 2) {
-      out[i] = E::from_float(acc[i] * inv);
+    for (int i = 0; i < DPL / 2; ++i)
+      w[i] = (unsigned)E::from_float(acc[2 * i] * inv) |
+             ((unsigned)E::from_float(acc[2 * i + 1] * inv) << 16);
+    if constexpr (DPL == 4) {
+      *reinterpret_cast<u32x2*>(out) = u32x2{w[0], w[1]};
     } else {
-      out[i] = acc[i] * inv;
+#pragma unroll
+      for (int i = 0; i < DPL / 2; i += 4)
+        *reinterpret_cast<u32x4*>(out + 2 * i) = u32x4{w[i], w[i + 1], w[i + 2], w[i + 3]};
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < DPL; i += 4)
+      *reinterpret_cast<f32x4*>(out + i) =
+          f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
   }
 }
 
