@@ -125,6 +125,15 @@ pa_status pa_decode(const pa_kv_cache *cache, void *out, const void *q,
  * split_tokens), at least 1. Returns 0 if split_tokens <= 0. */
 int pa_splitk_num_splits(int max_seq_len, int split_tokens);
 
+/* Bytes of the split-K partials for these sizes [P1 §07]: o_part
+ * (B * Hq * S * D floats) followed by lse_part (B * Hq * S floats), with
+ * S = pa_splitk_num_splits(max_seq_len, split_tokens). A caller may carve both
+ * from one buffer of this size: o_part at its start, lse_part at float
+ * offset B * Hq * S * D. Returns 0 when an argument is negative, head_dim or
+ * num_heads is not positive, or split_tokens <= 0. */
+size_t pa_splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_seq_len,
+                                 int split_tokens);
+
 /* Split-K (Flash-Decoding) partials [P1 §07]: split j of request r covers
  * tokens [j*split_tokens, min((j+1)*split_tokens, seq_len)).
  *   o_part   : fp32 [B, Hq, S, D]; split j's softmax-normalised output

@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     pa_lse_merge,
     pa_rope_write_kv,
     pa_splitk_num_splits,
+    pa_splitk_workspace_bytes,
     pa_status_str,
     pa_varlen,
     pa_varlen_workspace_bytes,

@@ -44,6 +44,7 @@ SIGNATURES = {
     "pa_write_kv": (_I, [_CACHE, _P, _P, _P, _I, _P]),
     "pa_decode": (_I, [_CACHE, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
     "pa_splitk_num_splits": (_I, [_I, _I]),
+    "pa_splitk_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "pa_decode_splitk": (_I, [_CACHE, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "pa_lse_merge": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pa_varlen_workspace_bytes": (ctypes.c_size_t, [_CACHE, _I, _I, _I, _I]),

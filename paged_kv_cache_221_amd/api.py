@@ -191,6 +191,14 @@ def pa_splitk_num_splits(max_seq_len: int, split_tokens: int) -> int:
     return int(_native.load().pa_splitk_num_splits(int(max_seq_len), int(split_tokens)))
 
 
+def pa_splitk_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_seq_len: int,
+                              split_tokens: int) -> int:
+    """Bytes of the split-K partials (o_part then lse_part, fp32)."""
+    return int(_native.load().pa_splitk_workspace_bytes(int(num_seqs), int(num_heads),
+                                                        int(head_dim), int(max_seq_len),
+                                                        int(split_tokens)))
+
+
 def pa_decode_splitk(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int,
                      split_tokens: int, scale: float, o_part=None, lse_part=None,
                      k_scale: float = 1.0, v_scale: float = 1.0):

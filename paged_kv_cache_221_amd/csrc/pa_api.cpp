@@ -341,6 +341,15 @@ int pa_splitk_num_splits(int max_seq_len, int split_tokens) {
   return s > 0 ? s : 1;
 }
 
+size_t pa_splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_seq_len,
+                                 int split_tokens) {
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || split_tokens <= 0)
+    return 0;
+  const size_t rows = (size_t)num_seqs * (size_t)num_heads *
+                      (size_t)pa_splitk_num_splits(max_seq_len, split_tokens);
+  return rows * (size_t)head_dim * sizeof(float) + rows * sizeof(float);
+}
+
 pa_status pa_decode_splitk(const pa_kv_cache* cache, float* o_part, float* lse_part,
                            const void* q, const int32_t* block_table, const int32_t* seq_lens,
                            int num_seqs, int num_heads, int max_blocks_per_seq, int max_seq_len,

@@ -2,7 +2,9 @@
 // runtime for device memory and a stream, no Python. It reads one decode
 // step's inputs from a directory of raw files, runs pa_write_kv and then
 // pa_decode_balanced on one stream with a caller-owned workspace (its
-// contents need not be initialised), and writes the output and both caches back to the directory.
+// contents need not be initialised), then the same attention as split-K
+// partials plus their merge in a workspace sized by pa_splitk_workspace_bytes,
+// and writes both outputs and both caches back to the directory.
 // It also checks one error path: a head count that is not a multiple of the
 // KV head count must be refused with PA_ERR_SHAPE before anything launches.
 // tests/test_gpu_c_abi.py builds the inputs and compares the results with the
@@ -108,17 +110,41 @@ int main(int argc, char** argv) {
   CHECK_PA(pa_decode_balanced(&cache, dout, dq, (const int32_t*)dbt, (const int32_t*)dlens,
                               num_seqs, num_heads, max_blocks, max_seq_len, scale, ws, ws_bytes,
                               stream));
+  // the same step's attention again as split-K partials and their LSE merge
+  // [P1 §07], both partial arrays carved from one workspace of
+  // pa_splitk_workspace_bytes bytes (lse_part at float offset B*Hq*S*D)
+  const int split_tokens = 64;
+  const int splits = pa_splitk_num_splits(max_seq_len, split_tokens);
+  const size_t sk_bytes =
+      pa_splitk_workspace_bytes(num_seqs, num_heads, d, max_seq_len, split_tokens);
+  const size_t o_floats = (size_t)num_seqs * num_heads * splits * d;
+  if (splits <= 0 || sk_bytes != (o_floats + (size_t)num_seqs * num_heads * splits) * 4)
+    return 8;
+  void* sk = nullptr;
+  CHECK_HIP(hipMalloc(&sk, sk_bytes));
+  float* o_part = static_cast<float*>(sk);
+  float* lse_part = o_part + o_floats;
+  void* dout_sk = nullptr;
+  CHECK_HIP(hipMalloc(&dout_sk, q.size()));
+  CHECK_PA(pa_decode_splitk(&cache, o_part, lse_part, dq, (const int32_t*)dbt,
+                            (const int32_t*)dlens, num_seqs, num_heads, max_blocks, max_seq_len,
+                            split_tokens, scale, stream));
+  CHECK_PA(pa_lse_merge(dout_sk, nullptr, o_part, lse_part, (const int32_t*)dlens, num_seqs,
+                        num_heads, d, max_seq_len, split_tokens, (pa_dtype)dtype, stream));
   CHECK_HIP(hipStreamSynchronize(stream));
 
-  std::vector<char> out(q.size()), k_after(k_cache.size()), v_after(v_cache.size());
+  std::vector<char> out(q.size()), out_sk(q.size()), k_after(k_cache.size()),
+      v_after(v_cache.size());
   CHECK_HIP(hipMemcpy(out.data(), dout, out.size(), hipMemcpyDeviceToHost));
+  CHECK_HIP(hipMemcpy(out_sk.data(), dout_sk, out_sk.size(), hipMemcpyDeviceToHost));
   CHECK_HIP(hipMemcpy(k_after.data(), dk, k_after.size(), hipMemcpyDeviceToHost));
   CHECK_HIP(hipMemcpy(v_after.data(), dv, v_after.size(), hipMemcpyDeviceToHost));
   write_file(dir + "/out.bin", out.data(), out.size());
+  write_file(dir + "/out_splitk.bin", out_sk.data(), out_sk.size());
   write_file(dir + "/k_after.bin", k_after.data(), k_after.size());
   write_file(dir + "/v_after.bin", v_after.data(), v_after.size());
 
-  for (void* p : {dk, dv, dkn, dvn, dslot, dq, dbt, dlens, dout, ws}) CHECK_HIP(hipFree(p));
+  for (void* p : {dk, dv, dkn, dvn, dslot, dq, dbt, dlens, dout, ws, sk, dout_sk}) CHECK_HIP(hipFree(p));
   CHECK_HIP(hipStreamDestroy(stream));
   std::printf("ok %d requests\n", num_seqs);
   return 0;

@@ -3,9 +3,11 @@
 tests/c_abi/decode_step.cpp (built by __graft_entry__.build()) includes only
 include/pa.h and the HIP runtime: it reads a decode step's inputs from raw
 files, runs pa_write_kv and pa_decode_balanced on a stream of its own with a
-workspace it allocates, and writes the output and both caches back. The
+workspace it allocates, then split-K partials and their merge in one buffer
+sized by pa_splitk_workspace_bytes, and writes the outputs and both caches
+back. The
 caches must equal the oracle's write bit for bit (NaN poison in the other
-slots included) and the output the oracle's attention within the bf16 bound.
+slots included) and both outputs the oracle's attention within the bf16 bound.
 The program also checks that an invalid head count is refused with
 PA_ERR_SHAPE before anything is launched.
 """
@@ -63,3 +65,7 @@ def test_c_program_runs_a_decode_step(gpu_lib, tmp_path):
     err = max_err(oracle.widen(out, "bf16"), want)
     print(f"C program: max|err| = {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+    out_sk = np.fromfile(tmp_path / "out_splitk.bin", dtype=np.uint16).reshape(q.shape)
+    err_sk = max_err(oracle.widen(out_sk, "bf16"), want)
+    print(f"C program, split-K + merge: max|err| = {err_sk:.3e}", flush=True)
+    assert err_sk <= TOL["bf16"]

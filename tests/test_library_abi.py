@@ -42,6 +42,18 @@ def test_splitk_num_splits(lib):
     assert lib.pa_splitk_num_splits(100, 0) == 0
 
 
+def test_splitk_workspace_bytes(lib):
+    # o_part [B, Hq, S, D] then lse_part [B, Hq, S], fp32: config 3's
+    # 8 requests x 32 heads x 64 splits of 2048 tokens, head_dim 128
+    assert lib.pa_splitk_workspace_bytes(8, 32, 128, 131072, 2048) == 8 * 32 * 64 * 129 * 4
+    assert lib.pa_splitk_workspace_bytes(3, 4, 64, 2049, 2048) == 3 * 4 * 2 * 65 * 4
+    assert lib.pa_splitk_workspace_bytes(0, 4, 64, 100, 16) == 0
+    assert lib.pa_splitk_workspace_bytes(1, 4, 64, 0, 16) == 4 * 65 * 4  # one (empty) split
+    for bad in ((-1, 4, 64, 100, 16), (1, 0, 64, 100, 16), (1, 4, 0, 100, 16),
+                (1, 4, 64, -1, 16), (1, 4, 64, 100, 0)):
+        assert lib.pa_splitk_workspace_bytes(*bad) == 0
+
+
 def test_validation_codes(lib):
     byref = ctypes.byref
     one = ctypes.c_void_p(1)
