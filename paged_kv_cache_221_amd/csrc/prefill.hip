@@ -55,6 +55,13 @@ namespace {
 #define PA_PREFILL_WAVES 4
 #endif
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;
+// Cache policy of the prefill's KV block loads (0: default; 2: nt). Several
+// workgroups (the tiles of one request) read the same blocks, so they are
+// not marked as streaming data by default.
+#ifndef PA_PF_LOAD_AUX
+#define PA_PF_LOAD_AUX 0
+#endif
+constexpr int kPfAux = PA_PF_LOAD_AUX;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 static_assert(PA_PREFILL_RING % 4 == 0, "the ring (halved for fp32) alternates two LDS buffers");
 
@@ -179,8 +186,8 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
       const int off = c < St::kChunks
                           ? (c / St::kChunksPerRow) * row_bytes_g + (c % St::kChunksPerRow) * 16
                           : 0x7ffffff0;
-      rg.k[p] = buf_load16(rk, off);
-      rg.v[p] = buf_load16(rv, off);
+      rg.k[p] = buf_load16<kPfAux>(rk, off);
+      rg.v[p] = buf_load16<kPfAux>(rv, off);
     }
   };
   auto stage = [&](const typename St::Regs& rg, int buf) {
