@@ -82,6 +82,13 @@ def check_cache_after_write(st, snap: Snapshot):
             assert np.array_equal(got_v[b], snap.v[b]), f"V block {b} differs"
 
 
+def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """Bitwise equality of two GPU tensors of one dtype (NaN payloads and
+    signed zeros included)."""
+    raw = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[a.element_size()]
+    return a.shape == b.shape and torch.equal(a.view(raw), b.view(raw))
+
+
 def max_err(got: np.ndarray, want: np.ndarray) -> float:
     if got.size == 0:
         return 0.0
@@ -110,12 +117,16 @@ def rel_err(got: np.ndarray, want: np.ndarray, groups) -> tuple[float, int]:
 
 def check_close(got: np.ndarray, want: np.ndarray, dtype: str, groups=None,
                 label: str = "") -> float:
-    """Both bounds: the absolute TOL over everything compared, and REL_TOL per
-    group (default: each index of axis 0, i.e. each decode request).
-    Returns the absolute error."""
+    """Both bounds over the rows of ``groups`` (default: each index of axis
+    0, i.e. each decode request; rows outside every group are not compared):
+    the absolute TOL over all of them, and REL_TOL per group. Returns the
+    absolute error."""
     if groups is None:
         groups = range(want.shape[0])
-    err = max_err(got, want)
+    groups = list(groups)
+    rows = np.concatenate([np.atleast_1d(np.asarray(g)).reshape(-1) for g in groups]) \
+        if groups else np.zeros(0, np.int64)
+    err = max_err(got[rows], want[rows])
     rel, where = rel_err(got, want, groups)
     print(f"{label}: max|err| = {err:.3e}, worst per-request relative = {rel:.3e}"
           f" (group {where})", flush=True)

@@ -19,7 +19,7 @@ from oracle.block_manager import copy_blocks as oracle_copy_blocks
 import paged_kv_cache_221_amd as pa
 from workloads.tensors import TORCH_DTYPES, raw_bits
 
-from _parity import TOL, gpu_rows, max_err
+from _parity import check_close, gpu_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -117,8 +117,8 @@ class _Run:
         q_bits = raw_bits(q, self.dtype)
         want, _ = oracle.paged_decode(q_bits, self.k_host, self.v_host, table_np, lens,
                                       self.scale, self.bs, self.dtype)
-        err = max_err(gpu_rows(out, self.dtype), want)
-        assert err <= TOL[self.dtype], err
+        err = check_close(gpu_rows(out, self.dtype), want, self.dtype,
+                          label="block manager decode")
         # the paged result is attention over the sequence's own history
         for i, s in enumerate(seqs):
             kh = oracle.widen(np.stack(self.hist[s][0]), self.dtype)

@@ -19,7 +19,7 @@ from oracle import fp8
 from workloads import small_decode
 from workloads.tensors import materialize, materialize_e4m3, raw_bits
 
-from _parity import TOL, gpu_rows, max_err
+from _parity import check_close, gpu_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -84,9 +84,7 @@ def test_fused_step_equals_write_then_decode(gpu_lib, case):
     ref, _ = oracle.paged_decode(raw_bits(st.q, adt), k_host, v_host, lay.block_table,
                                  lens.cpu().numpy(), lay.scale, lay.block_size, adt,
                                  requests=keep, **extra)
-    err = max_err(gpu_rows(got, adt)[keep], ref[keep])
-    print(f"{lay.name} {dtype} fused: max|err| = {err:.3e}", flush=True)
-    assert err <= TOL[adt]
+    check_close(gpu_rows(got, adt)[keep], ref[keep], adt, label=f"{lay.name} {dtype} fused")
     assert torch.all(got[4] == 0)
 
 

@@ -2,7 +2,6 @@
 
 import numpy as np
 import pytest
-import torch
 
 import oracle
 from workloads import (BENCH_CONFIGS, llama2_7b_mha_decode, llama3_8b_decode,
