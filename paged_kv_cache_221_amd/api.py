@@ -4,8 +4,11 @@ Each function checks that the torch tensors it is handed are contiguous GPU
 tensors with the dtypes and shapes ``include/pa.h`` requires, passes their
 device pointers and torch's current stream to ``libpa.so``, and raises
 ``PaError`` on a non-OK status. Output tensors are allocated with torch when
-the caller does not pass them. No step of the computation happens here, and
-there is no CPU fallback.
+the caller does not pass them. With ``prepared=True`` a function does the
+checks and the marshalling and returns a ``PreparedCall`` that issues the
+same call each time it is called (a serving loop's or a benchmark's repeated
+step, without the per-call checks). No step of the computation happens here,
+and there is no CPU fallback.
 """
 
 from __future__ import annotations
@@ -53,8 +56,37 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+class PreparedCall:
+    """One entry point with its tensors checked and its arguments marshalled
+    once. Each call issues it again, with the same arguments, on the device's
+    current stream (looked up per call, so a call made while a HIP graph is
+    being captured lands on the capturing stream), and returns what the
+    one-shot call returns. It holds a reference to every tensor it points at;
+    their contents may change between calls, their storage must not."""
+
+    __slots__ = ("name", "_fn", "_args", "_device", "_keep", "result")
+
+    def __init__(self, name: str, args: list, device, keep, result):
+        self.name = name
+        self._fn = getattr(_native.load(), name)
+        self._args = args
+        self._device = device
+        self._keep = keep
+        self.result = result
+
+    def __call__(self):
+        self._args[-1] = torch.cuda.current_stream(self._device).cuda_stream
+        status = self._fn(*self._args)
+        if status != _native.PA_OK:
+            raise PaError(self.name, status)
+        return self.result
+
+
+def _issue(name: str, args: list, device, prepared: bool, keep, result=None):
+    """Issue the call now (stream: the device's current one), or return it as
+    a PreparedCall. ``args`` ends with a placeholder for the stream."""
+    call = PreparedCall(name, args, device, keep, result)
+    return call if prepared else call()
 
 
 def kv_cache_struct(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float = 1.0,
@@ -80,8 +112,7 @@ def pa_status_str(status: int) -> str:
 
 
 def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, k_scale: float = 1.0,
-                v_scale: float = 1.0) -> None:
-    lib = _native.load()
+                v_scale: float = 1.0, prepared: bool = False):
     c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
     t = slot_mapping.shape[0]
     _dev(slot_mapping, "slot_mapping", torch.int64)
@@ -89,8 +120,9 @@ def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, k_scale: float = 1
         _dev(x, name, _act_dtype(k_cache))
         if tuple(x.shape) != (t, c.num_kv_heads, c.head_dim):
             raise ValueError(f"{name} must be [num_tokens, Hkv, D]")
-    _check("pa_write_kv", lib.pa_write_kv(ctypes.byref(c), _ptr(k_new), _ptr(v_new),
-                                          _ptr(slot_mapping), t, _stream(k_cache)))
+    return _issue("pa_write_kv", [ctypes.byref(c), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                                  t, None], k_cache.device, prepared,
+                  (c, k_cache, v_cache, k_new, v_new, slot_mapping))
 
 
 def _attention_meta(c, block_table, seq_lens, num_seqs):
@@ -104,8 +136,7 @@ def _attention_meta(c, block_table, seq_lens, num_seqs):
 
 
 def pa_decode(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int, scale: float,
-              out=None, k_scale: float = 1.0, v_scale: float = 1.0):
-    lib = _native.load()
+              out=None, k_scale: float = 1.0, v_scale: float = 1.0, prepared: bool = False):
     c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
     _dev(q, "q", _act_dtype(k_cache))
     if q.dim() != 3 or q.shape[2] != c.head_dim:
@@ -115,10 +146,10 @@ def pa_decode(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int, scal
     out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
-    _check("pa_decode", lib.pa_decode(ctypes.byref(c), _ptr(out), _ptr(q), _ptr(block_table),
-                                      _ptr(seq_lens), b, hq, max_blocks, int(max_seq_len),
-                                      float(scale), _stream(q)))
-    return out
+    return _issue("pa_decode", [ctypes.byref(c), _ptr(out), _ptr(q), _ptr(block_table),
+                                _ptr(seq_lens), b, hq, max_blocks, int(max_seq_len),
+                                float(scale), None], q.device, prepared,
+                  (c, k_cache, v_cache, q, block_table, seq_lens, out), out)
 
 
 def pa_decode_balanced_workspace_bytes(k_cache, v_cache, num_seqs: int, num_heads: int) -> int:
@@ -129,11 +160,10 @@ def pa_decode_balanced_workspace_bytes(k_cache, v_cache, num_seqs: int, num_head
 
 def pa_decode_balanced(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int,
                        scale: float, workspace=None, out=None, k_scale: float = 1.0,
-                       v_scale: float = 1.0):
+                       v_scale: float = 1.0, prepared: bool = False):
     """Balanced decode; ``workspace`` is a uint8 GPU tensor of at least
     ``pa_decode_balanced_workspace_bytes`` bytes (allocated here if None); its
     contents need not be initialised."""
-    lib = _native.load()
     c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
     _dev(q, "q", _act_dtype(k_cache))
     if q.dim() != 3 or q.shape[2] != c.head_dim:
@@ -147,19 +177,17 @@ def pa_decode_balanced(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: 
     out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
-    _check("pa_decode_balanced", lib.pa_decode_balanced(
+    return _issue("pa_decode_balanced", [
         ctypes.byref(c), _ptr(out), _ptr(q), _ptr(block_table), _ptr(seq_lens), b, hq,
-        max_blocks, int(max_seq_len), float(scale), _ptr(workspace), workspace.numel(),
-        _stream(q)))
-    return out
+        max_blocks, int(max_seq_len), float(scale), _ptr(workspace), workspace.numel(), None],
+        q.device, prepared, (c, k_cache, v_cache, q, block_table, seq_lens, workspace, out), out)
 
 
 def pa_write_decode_balanced(k_cache, v_cache, q, k_new, v_new, slot_mapping, block_table,
                              seq_lens, max_seq_len: int, scale: float, workspace=None, out=None,
-                             k_scale: float = 1.0, v_scale: float = 1.0):
+                             k_scale: float = 1.0, v_scale: float = 1.0, prepared: bool = False):
     """A decode step in one call: pa_write_kv of k_new/v_new [B, Hkv, D] to
     slot_mapping [B] fused into pa_decode_balanced (see include/pa.h)."""
-    lib = _native.load()
     c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
     _dev(q, "q", _act_dtype(k_cache))
     if q.dim() != 3 or q.shape[2] != c.head_dim:
@@ -180,11 +208,12 @@ def pa_write_decode_balanced(k_cache, v_cache, q, k_new, v_new, slot_mapping, bl
     out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
-    _check("pa_write_decode_balanced", lib.pa_write_decode_balanced(
+    return _issue("pa_write_decode_balanced", [
         ctypes.byref(c), _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
         _ptr(block_table), _ptr(seq_lens), b, hq, max_blocks, int(max_seq_len), float(scale),
-        _ptr(workspace), workspace.numel(), _stream(q)))
-    return out
+        _ptr(workspace), workspace.numel(), None], q.device, prepared,
+        (c, k_cache, v_cache, q, k_new, v_new, slot_mapping, block_table, seq_lens, workspace,
+         out), out)
 
 
 def pa_splitk_num_splits(max_seq_len: int, split_tokens: int) -> int:
@@ -201,8 +230,7 @@ def pa_splitk_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_
 
 def pa_decode_splitk(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: int,
                      split_tokens: int, scale: float, o_part=None, lse_part=None,
-                     k_scale: float = 1.0, v_scale: float = 1.0):
-    lib = _native.load()
+                     k_scale: float = 1.0, v_scale: float = 1.0, prepared: bool = False):
     c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
     _dev(q, "q", _act_dtype(k_cache))
     if q.dim() != 3 or q.shape[2] != c.head_dim:
@@ -218,16 +246,16 @@ def pa_decode_splitk(k_cache, v_cache, q, block_table, seq_lens, max_seq_len: in
     _dev(lse_part, "lse_part", torch.float32)
     if s > 0 and (tuple(o_part.shape) != (b, hq, s, d) or tuple(lse_part.shape) != (b, hq, s)):
         raise ValueError(f"o_part/lse_part must be [B, Hq, {s}, D] / [B, Hq, {s}]")
-    _check("pa_decode_splitk", lib.pa_decode_splitk(
+    return _issue("pa_decode_splitk", [
         ctypes.byref(c), _ptr(o_part), _ptr(lse_part), _ptr(q), _ptr(block_table),
         _ptr(seq_lens), b, hq, max_blocks, int(max_seq_len), int(split_tokens), float(scale),
-        _stream(q)))
-    return o_part, lse_part
+        None], q.device, prepared,
+        (c, k_cache, v_cache, q, block_table, seq_lens, o_part, lse_part), (o_part, lse_part))
 
 
 def pa_lse_merge(o_part, lse_part, seq_lens, max_seq_len: int, split_tokens: int,
-                 out_dtype=torch.float32, out=None, lse_out=None, want_lse: bool = False):
-    lib = _native.load()
+                 out_dtype=torch.float32, out=None, lse_out=None, want_lse: bool = False,
+                 prepared: bool = False):
     _dev(o_part, "o_part", torch.float32)
     _dev(lse_part, "lse_part", torch.float32)
     _dev(seq_lens, "seq_lens", torch.int32)
@@ -244,10 +272,11 @@ def pa_lse_merge(o_part, lse_part, seq_lens, max_seq_len: int, split_tokens: int
         lse_out = torch.empty((b, hq), dtype=torch.float32, device=o_part.device)
     if lse_out is not None:
         _dev(lse_out, "lse_out", torch.float32)
-    _check("pa_lse_merge", lib.pa_lse_merge(
+    return _issue("pa_lse_merge", [
         _ptr(out), _ptr(lse_out), _ptr(o_part), _ptr(lse_part), _ptr(seq_lens), b, hq, d,
-        int(max_seq_len), int(split_tokens), _DTYPE_CODE[out_dtype], _stream(o_part)))
-    return (out, lse_out) if lse_out is not None else out
+        int(max_seq_len), int(split_tokens), _DTYPE_CODE[out_dtype], None], o_part.device,
+        prepared, (out, lse_out, o_part, lse_part, seq_lens),
+        (out, lse_out) if lse_out is not None else out)
 
 
 def pa_varlen_workspace_bytes(k_cache, v_cache, num_seqs: int, num_tokens: int,
@@ -260,12 +289,11 @@ def pa_varlen_workspace_bytes(k_cache, v_cache, num_seqs: int, num_tokens: int,
 
 def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_query_len: int,
               max_seq_len: int, scale: float, causal: bool = True, out=None, workspace="auto",
-              k_scale: float = 1.0, v_scale: float = 1.0):
+              k_scale: float = 1.0, v_scale: float = 1.0, prepared: bool = False):
     """Varlen step. ``workspace``: "auto" allocates one of
     ``pa_varlen_workspace_bytes`` bytes (the balanced path for single-tile
     requests), None passes NULL (one workgroup per request and KV head), or a
     uint8 GPU tensor."""
-    lib = _native.load()
     c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
     _dev(q, "q", _act_dtype(k_cache))
     if q.dim() != 3 or q.shape[2] != c.head_dim:
@@ -286,20 +314,19 @@ def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_quer
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
-    _check("pa_varlen", lib.pa_varlen(
+    return _issue("pa_varlen", [
         ctypes.byref(c), _ptr(out), _ptr(q), _ptr(cu_seqlens_q), _ptr(seq_lens),
         _ptr(block_table), b, t, hq, max_blocks, int(max_query_len), int(max_seq_len),
         float(scale), 1 if causal else 0, _ptr(workspace),
-        workspace.numel() if workspace is not None else 0, _stream(q)))
-    return out
+        workspace.numel() if workspace is not None else 0, None], q.device, prepared,
+        (c, k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, workspace, out), out)
 
 
 def pa_rope_write_kv(k_cache, v_cache, q, k_new, v_new, slot_mapping, positions, cos_sin,
-                     rotary_dim: int, neox_style: bool = True) -> None:
+                     rotary_dim: int, neox_style: bool = True, prepared: bool = False):
     """Rotary embedding fused with the KV write: q [T, Hq, D] is rotated in
     place, the rotated k_new and v_new [T, Hkv, D] go to slot_mapping.
     ``positions`` int32 [T], ``cos_sin`` fp32 [max_position, rotary_dim]."""
-    lib = _native.load()
     c = kv_cache_struct(k_cache, v_cache)
     _dev(q, "q", _act_dtype(k_cache))
     t = slot_mapping.shape[0]
@@ -314,22 +341,22 @@ def pa_rope_write_kv(k_cache, v_cache, q, k_new, v_new, slot_mapping, positions,
             raise ValueError(f"{name} must be [num_tokens, Hkv, D]")
     if tuple(positions.shape) != (t,) or cos_sin.dim() != 2 or cos_sin.shape[1] != rotary_dim:
         raise ValueError("positions must be [T] and cos_sin [max_position, rotary_dim]")
-    _check("pa_rope_write_kv", lib.pa_rope_write_kv(
+    return _issue("pa_rope_write_kv", [
         ctypes.byref(c), _ptr(q), int(q.shape[1]), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
         _ptr(positions), _ptr(cos_sin), int(cos_sin.shape[0]), int(rotary_dim),
-        1 if neox_style else 0, t, _stream(q)))
+        1 if neox_style else 0, t, None], q.device, prepared,
+        (c, k_cache, v_cache, q, k_new, v_new, slot_mapping, positions, cos_sin))
 
 
-def pa_copy_blocks(k_cache, v_cache, src_dst) -> None:
+def pa_copy_blocks(k_cache, v_cache, src_dst, prepared: bool = False):
     """Copy-on-write block copies: ``src_dst`` is an int32 GPU tensor
     [num_pairs, 2] of (source, destination) blocks."""
-    lib = _native.load()
     c = kv_cache_struct(k_cache, v_cache)
     _dev(src_dst, "src_dst", torch.int32)
     if src_dst.dim() != 2 or src_dst.shape[1] != 2:
         raise ValueError("src_dst must be [num_pairs, 2]")
-    _check("pa_copy_blocks", lib.pa_copy_blocks(ctypes.byref(c), _ptr(src_dst),
-                                                int(src_dst.shape[0]), _stream(k_cache)))
+    return _issue("pa_copy_blocks", [ctypes.byref(c), _ptr(src_dst), int(src_dst.shape[0]), None],
+                  k_cache.device, prepared, (c, k_cache, v_cache, src_dst))
 
 
 class BlockManager:
