@@ -20,6 +20,9 @@ LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
 SOURCES = ["attention.hip", "balanced.hip", "prefill.hip", "write_kv.hip", "lse_merge.hip",
            "block_manager.cpp",
            "pa_api.cpp"]
+# the benchmark's HBM read ceilings (include/pa_probe.h), a library of its own
+PROBE_SOURCES = ["hbm_probe.hip"]
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libpa_probe.so")
 ARCH = "gfx950"
 
 
@@ -51,6 +54,16 @@ def _compile(src: str, build_dir: str = BUILD_DIR, extra=()) -> str:
     return obj
 
 
+def _link(objs, lib_path: str) -> None:
+    tmp = lib_path + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking {os.path.basename(lib_path)} failed:\n{res.stdout}\n"
+                           f"{res.stderr}")
+    os.replace(tmp, lib_path)
+
+
 def build(jobs: int = 4, extra_flags=(), lib_path: str = LIB_PATH,
           build_dir: str = BUILD_DIR) -> str:
     """Compile and link; ``extra_flags`` (e.g. ``-DPA_KV_DEPTH=3``) override
@@ -58,14 +71,17 @@ def build(jobs: int = 4, extra_flags=(), lib_path: str = LIB_PATH,
     os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as pool:
         objs = list(pool.map(lambda src: _compile(src, build_dir, tuple(extra_flags)), SOURCES))
-    tmp = lib_path + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"linking libpa.so failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, lib_path)
+    _link(objs, lib_path)
     return lib_path
+
+
+def build_probe(build_dir: str = BUILD_DIR) -> str:
+    """The benchmark's read-ceiling library, libpa_probe.so."""
+    os.makedirs(build_dir, exist_ok=True)
+    _link([_compile(src, build_dir) for src in PROBE_SOURCES], PROBE_LIB_PATH)
+    return PROBE_LIB_PATH
 
 
 if __name__ == "__main__":
     print(build())
+    print(build_probe())
