@@ -64,7 +64,7 @@ typedef enum {
   PA_ERR_SHAPE = -2,       /* inconsistent or negative sizes */
   PA_ERR_DTYPE = -3,       /* unknown dtype */
   PA_ERR_UNSUPPORTED = -4, /* valid but not implemented (see above) */
-  PA_ERR_WORKSPACE = -5,   /* split-K workspace arguments inconsistent */
+  PA_ERR_WORKSPACE = -5,   /* workspace too small, or split-K workspace arguments inconsistent */
   PA_ERR_LAUNCH = -6,      /* the HIP runtime rejected a kernel launch */
   PA_ERR_NO_BLOCKS = -7,   /* block manager: the pool has too few free blocks */
   PA_ERR_SEQUENCE = -8,    /* block manager: unknown (or, for a fork, existing) id */
@@ -207,6 +207,29 @@ pa_status pa_write_decode_balanced(const pa_kv_cache *cache, void *out, const vo
                                    const int32_t *seq_lens, int num_seqs, int num_heads,
                                    int max_blocks_per_seq, int max_seq_len, float scale,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* pa_write_decode_balanced for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, bit for bit, with the workspace
+ * taken from a scratch array the library holds in device memory, one per GPU
+ * it runs on, of PA_NOALLOC_SCRATCH_BYTES bytes (16 MiB), kept until the
+ * process ends. The call allocates nothing; its first call on
+ * a device looks up that device's copy of the array. A batch whose workspace
+ * (pa_decode_balanced_workspace_bytes) exceeds the scratch returns
+ * PA_ERR_WORKSPACE and launches nothing; the Llama-3-8B decode shape (32
+ * query / 8 KV heads, head_dim 128) fits up to about 750 requests. The
+ * scratch needs no clearing between calls (every call writes what it later
+ * reads), but it is shared by every call on one GPU: calls that may overlap
+ * on one GPU (several streams, several host threads) race and must not be
+ * issued; use pa_write_decode_balanced with separate workspaces for that.
+ * Arguments as for pa_write_decode_balanced, less the workspace. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+pa_status pa_write_decode_balanced_noalloc(const pa_kv_cache *cache, void *out, const void *q,
+                                           const void *k_new, const void *v_new,
+                                           const int64_t *slot_mapping,
+                                           const int32_t *block_table, const int32_t *seq_lens,
+                                           int num_seqs, int num_heads, int max_blocks_per_seq,
+                                           int max_seq_len, float scale, void *stream);
 
 /* Varlen mixed step [P1 §03/§04 flattened batch and cu_seqlens; P1 §07
  * chunked prefill]: request r owns query rows [cu[r], cu[r+1]) of the

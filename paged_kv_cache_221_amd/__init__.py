@@ -23,6 +23,7 @@ from .api import (  # noqa: F401
     pa_varlen,
     pa_varlen_workspace_bytes,
     pa_write_decode_balanced,
+    pa_write_decode_balanced_noalloc,
     pa_write_kv,
 )
 from .validate import PaMetadataError, validate_metadata  # noqa: F401

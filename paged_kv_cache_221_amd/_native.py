@@ -15,6 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
                       "include", "pa.h")
 
 PA_OK = 0
+PA_NOALLOC_SCRATCH_BYTES = 16 << 20   # include/pa.h
 PA_ERR_NO_BLOCKS = -7
 PA_ERR_SEQUENCE = -8
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
@@ -56,6 +57,8 @@ SIGNATURES = {
                                 _P]),
     "pa_write_decode_balanced": (_I, [_CACHE, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P,
                                       ctypes.c_size_t, _P]),
+    "pa_write_decode_balanced_noalloc": (_I, [_CACHE, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                              _F, _P]),
     "pa_copy_blocks": (_I, [_CACHE, _P, _I, _P]),
     "pa_rope_write_kv": (_I, [_CACHE, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "pa_bm_create": (_P, [_I, _I]),

@@ -216,6 +216,37 @@ def pa_write_decode_balanced(k_cache, v_cache, q, k_new, v_new, slot_mapping, bl
          out), out)
 
 
+def pa_write_decode_balanced_noalloc(k_cache, v_cache, q, k_new, v_new, slot_mapping,
+                                     block_table, seq_lens, max_seq_len: int, scale: float, out,
+                                     k_scale: float = 1.0, v_scale: float = 1.0,
+                                     prepared: bool = False):
+    """pa_write_decode_balanced with the library's per-GPU scratch instead of
+    a workspace: nothing is allocated, here or in the library, so ``out``
+    [B, Hq, D] must be given. Calls that may overlap on one GPU race on the
+    scratch (see include/pa.h)."""
+    c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
+    _dev(q, "q", _act_dtype(k_cache))
+    if q.dim() != 3 or q.shape[2] != c.head_dim:
+        raise ValueError("q must be [num_seqs, Hq, D]")
+    b, hq, _ = q.shape
+    max_blocks = _attention_meta(c, block_table, seq_lens, b)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    if tuple(slot_mapping.shape) != (b,):
+        raise ValueError("slot_mapping must be [num_seqs]")
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        _dev(x, name, _act_dtype(k_cache))
+        if tuple(x.shape) != (b, c.num_kv_heads, c.head_dim):
+            raise ValueError(f"{name} must be [num_seqs, Hkv, D]")
+    _dev(out, "out", q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    return _issue("pa_write_decode_balanced_noalloc", [
+        ctypes.byref(c), _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+        _ptr(block_table), _ptr(seq_lens), b, hq, max_blocks, int(max_seq_len), float(scale),
+        None], q.device, prepared,
+        (c, k_cache, v_cache, q, k_new, v_new, slot_mapping, block_table, seq_lens, out), out)
+
+
 def pa_splitk_num_splits(max_seq_len: int, split_tokens: int) -> int:
     return int(_native.load().pa_splitk_num_splits(int(max_seq_len), int(split_tokens)))
 

@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "pa_launch.h"
 
@@ -246,6 +247,36 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, const void* q, co
   return launched(pa::launch_balanced(a, cache->dtype, static_cast<hipStream_t>(stream)));
 }
 
+// Scratch of pa_write_decode_balanced_noalloc: the balanced kernels'
+// workspace (merge records, partial outputs and LSEs) for callers that cannot
+// allocate. Every GPU the library runs on holds its own copy until the
+// process ends. The array's name in host code is a host-side stand-in: its
+// device address on the current device comes from hipGetSymbolAddress, once
+// per device, and only that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch's device address on the current device (nullptr if the device
+// cannot be queried or the symbol lookup fails).
+void* scratch_device_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+      return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,7 +288,7 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_SHAPE: return "inconsistent or invalid sizes";
     case PA_ERR_DTYPE: return "unknown dtype";
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
-    case PA_ERR_WORKSPACE: return "split-K workspace arguments are inconsistent";
+    case PA_ERR_WORKSPACE: return "workspace too small, or split-K workspace arguments inconsistent";
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_NO_BLOCKS: return "not enough free KV blocks";
     case PA_ERR_SEQUENCE: return "unknown or duplicate sequence id";
@@ -529,6 +560,30 @@ pa_status pa_decode_balanced(const pa_kv_cache* cache, void* out, const void* q,
   return decode_balanced(cache, out, q, nullptr, nullptr, nullptr, block_table, seq_lens,
                          num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale, workspace,
                          workspace_bytes, stream);
+}
+
+pa_status pa_write_decode_balanced_noalloc(const pa_kv_cache* cache, void* out, const void* q,
+                                           const void* k_new, const void* v_new,
+                                           const int64_t* slot_mapping,
+                                           const int32_t* block_table, const int32_t* seq_lens,
+                                           int num_seqs, int num_heads, int max_blocks_per_seq,
+                                           int max_seq_len, float scale, void* stream) {
+  // the same checks as the workspace form, in the same order, before the
+  // scratch is looked up
+  pa_status s = check_cache(cache);
+  if (s != PA_OK) return s;
+  s = check_attention_shape(cache, num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale);
+  if (s != PA_OK) return s;
+  if (num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
+  if (pa_decode_balanced_workspace_bytes(cache, num_seqs, num_heads) > kScratchBytes)
+    return PA_ERR_WORKSPACE;
+  void* ws = scratch_device_ptr();
+  if (ws == nullptr) return PA_ERR_LAUNCH;
+  return decode_balanced(cache, out, q, k_new, v_new, slot_mapping, block_table, seq_lens,
+                         num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale, ws,
+                         kScratchBytes, stream);
 }
 
 pa_status pa_write_decode_balanced(const pa_kv_cache* cache, void* out, const void* q,
