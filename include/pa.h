@@ -130,7 +130,8 @@ int pa_splitk_num_splits(int max_seq_len, int split_tokens);
  * S = pa_splitk_num_splits(max_seq_len, split_tokens). A caller may carve both
  * from one buffer of this size: o_part at its start, lse_part at float
  * offset B * Hq * S * D. Returns 0 when an argument is negative, head_dim or
- * num_heads is not positive, or split_tokens <= 0. */
+ * num_heads is not positive, split_tokens <= 0, or the size does not fit in a
+ * size_t. */
 size_t pa_splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_seq_len,
                                  int split_tokens);
 

@@ -8,6 +8,7 @@ library is written next to this file and replaced atomically.
 from __future__ import annotations
 
 import os
+import shlex
 import shutil
 import subprocess
 from concurrent.futures import ThreadPoolExecutor
@@ -73,6 +74,43 @@ def build(jobs: int = 4, extra_flags=(), lib_path: str = LIB_PATH,
         objs = list(pool.map(lambda src: _compile(src, build_dir, tuple(extra_flags)), SOURCES))
     _link(objs, lib_path)
     return lib_path
+
+
+# Host code checked under sanitizers on the CPU: the block manager and the C
+# API's validation and sizing. Host-only instrumentation (each flag behind
+# -Xarch_host): device code is compiled as usual.
+HOST_SANITIZED_SOURCES = ("block_manager.cpp", "pa_api.cpp")
+HOST_SANITIZE_FLAGS = shlex.split(
+    "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+    "-Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer -O1")
+SANITIZE_DIR = os.path.join(BUILD_DIR, "sanitize")
+HOST_CHECKS = os.path.join(ROOT, "tests", "c_abi", "host_checks.cpp")
+
+
+def build_host_sanitized(build_dir: str = SANITIZE_DIR) -> str:
+    """libpa with AddressSanitizer and UndefinedBehaviorSanitizer on the host
+    code of HOST_SANITIZED_SOURCES (the kernels' sources as usual), and the
+    CPU program tests/c_abi/host_checks.cpp linked against it with the
+    sanitizer runtimes. Returns the program's path; running it needs no GPU."""
+    os.makedirs(build_dir, exist_ok=True)
+    objs = [_compile(src, build_dir, tuple(HOST_SANITIZE_FLAGS)
+                     if src in HOST_SANITIZED_SOURCES else ())
+            for src in SOURCES]
+    lib = os.path.join(build_dir, "libpa_host_sanitized.so")
+    _link(objs, lib)
+    exe = os.path.join(build_dir, "host_checks")
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin",
+                         "clang++")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang++"
+    cmd = [clang, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", os.path.join(ROOT, "include"), HOST_CHECKS, "-o", exe,
+           lib, "-Wl,-rpath," + build_dir]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking host_checks failed:\n{res.stdout}\n{res.stderr}")
+    return exe
 
 
 def build_probe(build_dir: str = BUILD_DIR) -> str:

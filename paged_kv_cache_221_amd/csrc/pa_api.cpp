@@ -2,6 +2,7 @@
 // sizing from host-known sizes and hints, and dispatch. Nothing here reads
 // device memory or synchronises.
 #include <math.h>
+#include <string.h>
 
 #include <atomic>
 #include <mutex>
@@ -15,8 +16,15 @@ using pa::AttnArgs;
 constexpr int kSupportedBlock = 16;
 constexpr int kMaxGroup = 16;
 
-bool dtype_ok(pa_dtype d) {
-  return d == PA_F32 || d == PA_F16 || d == PA_BF16 || d == PA_FP8_E4M3;
+// Whether a caller's dtype value names a storage type. A C caller may store
+// any integer in a pa_dtype; its bytes are read as an int (loading a value
+// outside the enumeration as the C++ enum type would be undefined), and only
+// a value that passes is used as a pa_dtype afterwards.
+bool dtype_ok(const pa_dtype& d) {
+  int v = -1;
+  static_assert(sizeof(pa_dtype) == sizeof(int), "pa_dtype is an int-sized enum");
+  memcpy(&v, &d, sizeof v);
+  return v == PA_F32 || v == PA_F16 || v == PA_BF16 || v == PA_FP8_E4M3;
 }
 // bytes of one cache element, and of one query / new-row / output element
 int kv_bytes(pa_dtype d) { return d == PA_F32 ? 4 : d == PA_FP8_E4M3 ? 1 : 2; }
@@ -281,7 +289,10 @@ void* scratch_device_ptr() {
 
 extern "C" {
 
-const char* pa_status_str(pa_status s) {
+const char* pa_status_str(pa_status status) {
+  // any integer may arrive here: read it as one (see dtype_ok)
+  int s = 0;
+  memcpy(&s, &status, sizeof s);
   switch (s) {
     case PA_OK: return "ok";
     case PA_ERR_NULL: return "a required pointer is NULL";
@@ -368,17 +379,24 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* q,
 
 int pa_splitk_num_splits(int max_seq_len, int split_tokens) {
   if (split_tokens <= 0) return 0;
-  const int s = (max_seq_len + split_tokens - 1) / split_tokens;
-  return s > 0 ? s : 1;
+  // in 64 bits: max_seq_len + split_tokens - 1 can pass INT_MAX
+  const int64_t s = ((int64_t)max_seq_len + split_tokens - 1) / split_tokens;
+  return s > 0 ? (int)s : 1;
 }
 
 size_t pa_splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_seq_len,
                                  int split_tokens) {
   if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || split_tokens <= 0)
     return 0;
-  const size_t rows = (size_t)num_seqs * (size_t)num_heads *
-                      (size_t)pa_splitk_num_splits(max_seq_len, split_tokens);
-  return rows * (size_t)head_dim * sizeof(float) + rows * sizeof(float);
+  // rows * (head_dim + 1) * 4 bytes; 0 if that does not fit in a size_t
+  size_t rows = 0, per_row = 0, bytes = 0;
+  if (__builtin_mul_overflow((size_t)num_seqs, (size_t)num_heads, &rows) ||
+      __builtin_mul_overflow(rows, (size_t)pa_splitk_num_splits(max_seq_len, split_tokens),
+                             &rows) ||
+      __builtin_mul_overflow((size_t)head_dim + 1, sizeof(float), &per_row) ||
+      __builtin_mul_overflow(rows, per_row, &bytes))
+    return 0;
+  return bytes;
 }
 
 pa_status pa_decode_splitk(const pa_kv_cache* cache, float* o_part, float* lse_part,
