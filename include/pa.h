@@ -42,10 +42,8 @@
  *   it copies the arrays from the device).
  * - Supported now: block_size 16; head_dim 64 or 128; Hq % Hkv == 0 with
  *   Hq / Hkv <= 16; fp32, fp16 and bf16 storage with fp32 accumulation, and
- *   E4M3 KV caches (bf16 arithmetic on the exactly widened codes) in
- *   pa_write_kv, pa_copy_blocks, pa_decode, pa_decode_splitk,
- *   pa_decode_balanced, pa_write_decode_balanced and pa_varlen batches
- *   without prefill chunks.
+ *   E4M3 KV caches (bf16 arithmetic on the exactly widened codes) in every
+ *   entry point.
  *   Anything else returns PA_ERR_UNSUPPORTED.
  */
 #ifndef PA_H
@@ -280,7 +278,10 @@ pa_status pa_varlen(const pa_kv_cache *cache, void *out, const void *q,
  *   positions  : device int32 [T]
  *   cos_sin    : device fp32 [max_position][rotary_dim] (cos | sin halves)
  *   rotary_dim : even, 2 .. head_dim
- *   neox_style : 1 pairs dimension i with i + rotary_dim/2, 0 pairs 2i with 2i+1 */
+ *   neox_style : 1 pairs dimension i with i + rotary_dim/2, 0 pairs 2i with 2i+1
+ * For an E4M3 cache q, k_new and v_new are bf16: q is rotated as for a bf16
+ * cache, and the rotated K row, rounded to bf16 as that path stores it, and
+ * the V row are quantised as pa_write_kv quantises a bf16 row. */
 pa_status pa_rope_write_kv(const pa_kv_cache *cache, void *q, int num_heads,
                            const void *k_new, const void *v_new,
                            const int64_t *slot_mapping, const int32_t *positions,

@@ -354,11 +354,13 @@ def pa_varlen(k_cache, v_cache, q, cu_seqlens_q, seq_lens, block_table, max_quer
 
 
 def pa_rope_write_kv(k_cache, v_cache, q, k_new, v_new, slot_mapping, positions, cos_sin,
-                     rotary_dim: int, neox_style: bool = True, prepared: bool = False):
+                     rotary_dim: int, neox_style: bool = True, k_scale: float = 1.0,
+                     v_scale: float = 1.0, prepared: bool = False):
     """Rotary embedding fused with the KV write: q [T, Hq, D] is rotated in
     place, the rotated k_new and v_new [T, Hkv, D] go to slot_mapping.
-    ``positions`` int32 [T], ``cos_sin`` fp32 [max_position, rotary_dim]."""
-    c = kv_cache_struct(k_cache, v_cache)
+    ``positions`` int32 [T], ``cos_sin`` fp32 [max_position, rotary_dim];
+    ``k_scale`` / ``v_scale``: an E4M3 cache's scales."""
+    c = kv_cache_struct(k_cache, v_cache, k_scale, v_scale)
     _dev(q, "q", _act_dtype(k_cache))
     t = slot_mapping.shape[0]
     _dev(slot_mapping, "slot_mapping", torch.int64)

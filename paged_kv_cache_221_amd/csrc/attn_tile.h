@@ -450,6 +450,26 @@ struct Ops<Fp8, D> : Ops16<Bf16, D> {
       }
     }
   }
+  // Same operand layout, from a block staged in LDS as codes (rows of
+  // `row_bytes` bytes, K rows then V rows in separate arrays).
+  __device__ static void load_lds(KV& kv, const char* kb, const char* vb, int row_bytes,
+                                  int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < kK16; ++j)
+      kv.k[j] = *reinterpret_cast<const u32x4*>(kb + m * row_bytes + 16 * (grp + 4 * j));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const char* src = vb + (4 * grp + i) * row_bytes + kVe * m;
+      if constexpr (kVe == 8) {
+        const u32x2 t = *reinterpret_cast<const u32x2*>(src);
+        kv.v[i][0] = t.x;
+        kv.v[i][1] = t.y;
+      } else {
+        kv.v[i][0] = *reinterpret_cast<const unsigned*>(src);
+      }
+    }
+  }
   __device__ static void load_q(Q& q, const uint16_t* qrow, bool valid, int lane) {
     const int grp = lane >> 4;
 #pragma unroll

@@ -139,7 +139,6 @@ struct PfSharesInit {
 } g_pf_shares_init;
 
 int prefill_shares(pa_dtype dtype, int head_dim) {
-  if (dtype == PA_FP8_E4M3) return 0;  // no prefill kernel for E4M3 caches
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
   if (dev >= kMaxDevices) return pa::prefill_resident_shares(dtype, head_dim);
@@ -332,7 +331,6 @@ pa_status pa_rope_write_kv(const pa_kv_cache* cache, void* q, int num_heads, con
   if (rotary_dim < 2 || rotary_dim % 2 != 0 || rotary_dim > cache->head_dim) return PA_ERR_SHAPE;
   if (neox_style != 0 && neox_style != 1) return PA_ERR_SHAPE;
   if (num_heads % cache->num_kv_heads != 0) return PA_ERR_SHAPE;
-  if (cache->dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
   if (q == nullptr || k_new == nullptr || v_new == nullptr || slot_mapping == nullptr ||
       positions == nullptr || cos_sin == nullptr)
@@ -503,7 +501,6 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
   // in equal shares over the resident workgroups when the workspace holds
   // their partials, else one workgroup per (tile, request, KV head)
   if ((int64_t)max_query_len * a.group > 16) {
-    if (cache->dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
     const int tt = pa::prefill_tile_tokens(cache->dtype, a.group);
     a.num_tiles = (max_query_len + tt - 1) / tt;
     if (use_ws && vl.pf_shares > 0) {

@@ -65,11 +65,12 @@ constexpr int kPfAux = PA_PF_LOAD_AUX;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 static_assert(PA_PREFILL_RING % 4 == 0, "the ring (halved for fp32) alternates two LDS buffers");
 
-// How one workgroup stages a block's head slice (16 keys) in LDS.
+// How one workgroup stages a block's head slice (16 keys) in LDS, in the
+// cache's storage type (E4M3 codes stay codes until the operands are built).
 template <class E, int D>
 struct Stage {
-  using S = typename Ops<E, D>::storage;
-  static constexpr int kRowBytes = D * (int)sizeof(S);      // one key's slice
+  using KS = typename Ops<E, D>::kv_storage;
+  static constexpr int kRowBytes = D * (int)sizeof(KS);     // one key's slice
   static constexpr int kLdsRow = kRowBytes + 16;            // padded: no bank conflicts
   static constexpr int kChunksPerRow = kRowBytes / 16;
   static constexpr int kChunks = kBlockTokens * kChunksPerRow;
@@ -137,7 +138,8 @@ template <class E, int D, int RT, int RING>
 __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfRequest& rq, int r,
                                 int kvh, int tile, int b0, int b1, int64_t slot) {
   using O = Ops<E, D>;
-  using S = typename O::storage;
+  using S = typename O::storage;       // q and outputs
+  using KS = typename O::kv_storage;   // the cache
   using St = Stage<E, D>;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -167,9 +169,9 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
   // staging of KV blocks: HBM -> registers (ring) -> LDS (two buffers)
   const int64_t rs = (int64_t)a.num_kv_heads * D;
   const int64_t block_elems = (int64_t)kBlockTokens * rs;
-  const int row_bytes_g = (int)(rs * (int64_t)sizeof(S));
-  const S* k_head = static_cast<const S*>(a.k_cache) + (int64_t)kvh * D;
-  const S* v_head = static_cast<const S*>(a.v_cache) + (int64_t)kvh * D;
+  const int row_bytes_g = (int)(rs * (int64_t)sizeof(KS));
+  const KS* k_head = static_cast<const KS*>(a.k_cache) + (int64_t)kvh * D;
+  const KS* v_head = static_cast<const KS*>(a.v_cache) + (int64_t)kvh * D;
   const __attribute__((address_space(4))) int32_t* tab =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)r * a.max_blocks);
   auto issue = [&](typename St::Regs& rg, int i) {
@@ -282,7 +284,9 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
     const int tok0 = tok_base + (wave * RT + rt) * tpw;
     const int tok = tok0 + row / g, hh = row - (row / g) * g;
     if (row < tpw * g && tok < n) {
-      const float inv = st[rt].l > 0.f ? 1.f / st[rt].l : 0.f;
+      // out_scale: an E4M3 cache's V scale (1 otherwise); partial rows carry
+      // it too, and the merge's weighted mean keeps it
+      const float inv = (st[rt].l > 0.f ? 1.f / st[rt].l : 0.f) * a.out_scale;
       if (slot < 0) {
         const int64_t orow = (int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh;
         S* dst = static_cast<S*>(a.out) + orow * D + (D / 4) * grp;
@@ -630,8 +634,9 @@ int prefill_resident_shares(pa_dtype dtype, int head_dim) {
     case PA_BF16: return head_dim == 128 ? resident_pf_shares<Bf16, 128>() : resident_pf_shares<Bf16, 64>();
     case PA_F16: return head_dim == 128 ? resident_pf_shares<F16, 128>() : resident_pf_shares<F16, 64>();
     case PA_F32: return head_dim == 128 ? resident_pf_shares<F32, 128>() : resident_pf_shares<F32, 64>();
-    default: return 0;
+    case PA_FP8_E4M3: return head_dim == 128 ? resident_pf_shares<Fp8, 128>() : resident_pf_shares<Fp8, 64>();
   }
+  return 0;
 }
 
 hipError_t launch_prefill(const AttnArgs& a, pa_dtype dtype, int head_dim, int64_t grid,
@@ -641,6 +646,7 @@ hipError_t launch_prefill(const AttnArgs& a, pa_dtype dtype, int head_dim, int64
       case PA_BF16: return head_dim == 128 ? launch_pf_shares<Bf16, 128>(a, stream) : launch_pf_shares<Bf16, 64>(a, stream);
       case PA_F16: return head_dim == 128 ? launch_pf_shares<F16, 128>(a, stream) : launch_pf_shares<F16, 64>(a, stream);
       case PA_F32: return head_dim == 128 ? launch_pf_shares<F32, 128>(a, stream) : launch_pf_shares<F32, 64>(a, stream);
+      case PA_FP8_E4M3: return head_dim == 128 ? launch_pf_shares<Fp8, 128>(a, stream) : launch_pf_shares<Fp8, 64>(a, stream);
       default: return hipErrorInvalidValue;
     }
   }
@@ -649,6 +655,7 @@ hipError_t launch_prefill(const AttnArgs& a, pa_dtype dtype, int head_dim, int64
     case PA_BF16: return head_dim == 128 ? launch_pf<Bf16, 128>(a, grid, stream) : launch_pf<Bf16, 64>(a, grid, stream);
     case PA_F16: return head_dim == 128 ? launch_pf<F16, 128>(a, grid, stream) : launch_pf<F16, 64>(a, grid, stream);
     case PA_F32: return head_dim == 128 ? launch_pf<F32, 128>(a, grid, stream) : launch_pf<F32, 64>(a, grid, stream);
+    case PA_FP8_E4M3: return head_dim == 128 ? launch_pf<Fp8, 128>(a, grid, stream) : launch_pf<Fp8, 64>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -674,6 +681,7 @@ hipError_t launch_prefill_merge(const AttnArgs& a, pa_dtype dtype, int head_dim,
     case PA_BF16: PA_PF_MERGE(Bf16) break;
     case PA_F16: PA_PF_MERGE(F16) break;
     case PA_F32: PA_PF_MERGE(F32) break;
+    case PA_FP8_E4M3: PA_PF_MERGE(Fp8) break;
     default: return hipErrorInvalidValue;
   }
 #undef PA_PF_MERGE

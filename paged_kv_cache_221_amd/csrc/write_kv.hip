@@ -179,6 +179,63 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_kv_kernel(
   for (int64_t i = threadIdx.x; i < row_elems; i += kWriteThreads) vd[i] = vs[i];
 }
 
+// The same step for an E4M3 cache: q is rotated in place as for a bf16
+// cache; the rotated K row, rounded to bf16 exactly as the bf16 path stores
+// it, and the V row are then quantised as pa_write_kv quantises a bf16 row
+// (x / scale in fp32, nearest E4M3 code, ties to even, saturating at 448).
+__global__ __launch_bounds__(kWriteThreads) void rope_write_kv_fp8_kernel(
+    uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping,
+    const int32_t* __restrict__ positions, const float* __restrict__ cos_sin, int max_position,
+    int rotary_dim, int neox, int num_heads, int num_kv_heads, int head_dim, int64_t num_slots,
+    float k_scale, float v_scale) {
+  const int64_t t = blockIdx.x;
+  const int pos = positions[t];
+  if (pos < 0 || pos >= max_position) return;  // outside the table: token left alone
+  const int half = rotary_dim / 2;
+  const float* cs = cos_sin + (int64_t)pos * rotary_dim;
+  auto pair = [&](int j, int* ia, int* ib) {
+    *ia = neox ? j : 2 * j;
+    *ib = neox ? j + half : 2 * j + 1;
+  };
+  auto code = [](uint16_t bf, float scale) {
+    return (uint8_t)e4m3_code(__fdiv_rn(__uint_as_float((unsigned)bf << 16), scale));
+  };
+  for (int i = threadIdx.x; i < num_heads * half; i += kWriteThreads) {
+    const int h = i / half, j = i - h * half;
+    int ia, ib;
+    pair(j, &ia, &ib);
+    uint16_t* row = q + (t * num_heads + h) * head_dim;
+    const float a = to_f32<Bf16>(row[ia]), b = to_f32<Bf16>(row[ib]);
+    const float c = cs[j], sn = cs[half + j];
+    row[ia] = from_f32<Bf16>(a * c - b * sn);
+    row[ib] = from_f32<Bf16>(b * c + a * sn);
+  }
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;  // padding token, or outside the pool
+  const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+  const uint16_t* ks = k_new + t * row_elems;
+  const uint16_t* vs = v_new + t * row_elems;
+  uint8_t* kd = k_cache + slot * row_elems;
+  uint8_t* vd = v_cache + slot * row_elems;
+  for (int i = threadIdx.x; i < num_kv_heads * half; i += kWriteThreads) {
+    const int h = i / half, j = i - h * half;
+    int ia, ib;
+    pair(j, &ia, &ib);
+    const float a = to_f32<Bf16>(ks[h * head_dim + ia]), b = to_f32<Bf16>(ks[h * head_dim + ib]);
+    const float c = cs[j], sn = cs[half + j];
+    kd[h * head_dim + ia] = code(from_f32<Bf16>(a * c - b * sn), k_scale);
+    kd[h * head_dim + ib] = code(from_f32<Bf16>(b * c + a * sn), k_scale);
+  }
+  const int rest = head_dim - rotary_dim;  // dimensions past rotary_dim: quantised as they are
+  for (int i = threadIdx.x; i < num_kv_heads * rest; i += kWriteThreads) {
+    const int h = i / rest, d = rotary_dim + (i - h * rest);
+    kd[h * head_dim + d] = code(ks[h * head_dim + d], k_scale);
+  }
+  for (int64_t i = threadIdx.x; i < row_elems; i += kWriteThreads) vd[i] = code(vs[i], v_scale);
+}
+
 // N consecutive floats from an address aligned to 4N bytes (N = 2, 4 or 8).
 template <int N>
 __device__ inline void load_floats(const float* p, float (&out)[N]) {
@@ -295,6 +352,15 @@ hipError_t launch_rope_write_kv(const pa_kv_cache* c, void* q, int num_heads, co
   if (num_tokens <= 0) return hipSuccess;
   const int64_t num_slots = (int64_t)c->num_blocks * c->block_size;
   const dim3 grid((unsigned)num_tokens), block(kWriteThreads);
+  if (c->dtype == PA_FP8_E4M3) {
+    rope_write_kv_fp8_kernel<<<grid, block, 0, stream>>>(
+        static_cast<uint16_t*>(q), static_cast<const uint16_t*>(k_new),
+        static_cast<const uint16_t*>(v_new), static_cast<uint8_t*>(c->k_cache),
+        static_cast<uint8_t*>(c->v_cache), slot_mapping, positions, cos_sin, max_position,
+        rotary_dim, neox, num_heads, c->num_kv_heads, c->head_dim, num_slots, c->k_scale,
+        c->v_scale);
+    return hipGetLastError();
+  }
   auto aligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   const bool vec = rotary_dim % 16 == 0 && c->head_dim % 8 == 0 && aligned(q) &&
                    aligned(k_new) && aligned(v_new) && aligned(c->k_cache) &&

@@ -12,8 +12,8 @@ bench.py times included, run from the unwritten, NaN-poisoned cache, and its
 E4M3-cache form), all eight long-context requests on the split-K path, 35
 requests of the 16 GiB MHA batch (the longest, both ends of the batch and
 the holders of the pool's first and last blocks among them), and for the
-mixed step the prefill chunks, sharers of the copy-on-write prefix and a
-seeded sample of decode rows.
+mixed step (bf16, and on an E4M3 cache) the prefill chunks, sharers of the
+copy-on-write prefix and a seeded sample of decode rows.
 """
 
 import numpy as np
@@ -242,6 +242,40 @@ def test_mixed_step_sampled(shuffled):
     assert len(rows) == 4 * 512 + len(req) - 4
     check_close(gpu_rows(out, lay.dtype), want, lay.dtype, groups=request_groups(lay, req),
                 label=f"{lay.name}: {len(req)} requests / {len(rows)} rows")
+
+
+def test_mixed_step_e4m3_sampled():
+    """The mixed continuous-batching step on an E4M3 cache (the bench's
+    scales): the quantising write of all 2,168 tokens bit-exact, the four
+    prefill chunks, three prefix sharers and a seeded sample of decode rows
+    against the oracle over the dequantised cache."""
+    lay = mixed_step()
+    ks, vs = E4M3_SCALES
+    st = materialize_e4m3(lay, "cuda", ks, vs)
+    k_host = raw_bits(st.k_cache, "e4m3").copy()
+    v_host = raw_bits(st.v_cache, "e4m3").copy()
+    q, kn, vn = raw_bits(st.q, "bf16"), raw_bits(st.k_new, "bf16"), raw_bits(st.v_new, "bf16")
+    pa.pa_write_kv(st.k_cache, st.v_cache, st.k_new, st.v_new, st.slot_mapping,
+                   k_scale=ks, v_scale=vs)
+    out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
+                       k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    fp8.write_kv(k_host, v_host, kn, vn, lay.slot_mapping, lay.block_size, ks, vs)
+    assert np.array_equal(raw_bits(st.k_cache, "e4m3"), k_host), "K codes differ"
+    assert np.array_equal(raw_bits(st.v_cache, "e4m3"), v_host), "V codes differ"
+    prefill = [r for r in range(lay.num_seqs) if lay.query_lens[r] > 1]
+    sharers = [r for r in range(lay.num_seqs)
+               if lay.query_lens[r] == 1 and np.array_equal(lay.block_table[r, :64],
+                                                            lay.shared_blocks)]
+    rng = np.random.Generator(np.random.PCG64(57))
+    others = [r for r in range(lay.num_seqs) if r not in prefill and r not in sharers]
+    req = sorted(set(prefill) | set(sharers[:3]) | set(rng.choice(others, 8, replace=False).tolist()))
+    want, _ = oracle.paged_varlen(q, k_host, v_host, lay.cu_seqlens_q, lay.seq_lens,
+                                  lay.block_table, lay.scale, lay.block_size, "bf16",
+                                  requests=req, kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    check_close(gpu_rows(out, "bf16"), want, "bf16", groups=request_groups(lay, req),
+                label=f"{lay.name} e4m3: {len(req)} requests")
 
 
 @pytest.mark.parametrize("query_len", [4, 8])

@@ -146,21 +146,111 @@ def test_fp8_varlen_decode_and_short_queries(gpu_lib, path):
                 label=f"{lay.name} e4m3 varlen {path}")
 
 
-def test_fp8_prefill_and_rope_are_refused(gpu_lib):
-    lay = small_varlen(975, dtype="bf16", num_heads=8, num_kv_heads=2, head_dim=128,
-                       prefill=((40, 0),), decode_lens=(5,))
-    s = _Fp8Step(lay, 0.1, 0.1)
+@pytest.mark.parametrize("path", ["shares", "per-tile"])
+@pytest.mark.parametrize("case", [(128, 32, 8), (64, 8, 2), (128, 16, 1)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_fp8_prefill_chunks(gpu_lib, case, path):
+    """Prefill chunks (several tiles, ragged ends, causal, with and without
+    cached context) beside decode rows on an E4M3 cache: codes staged in LDS
+    and widened exactly into the bf16 operands, V scale on every row (whole
+    tiles and the partial rows of cut ones)."""
+    d, hq, hkv = case
+    lay = small_varlen(975 + d + hq, dtype="bf16", num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       prefill=((40, 0), (130, 300), (65, 17), (9, 900)),
+                       decode_lens=(5, 333, 1))
+    s = _Fp8Step(lay, 0.0625, 0.045)
+    s.write()
     st = s.st
-    with pytest.raises(pa.PaError) as e:
-        pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
-                     st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale, **s.kw())
-    assert e.value.status == -4
-    cos_sin = torch.ones((64, 128), dtype=torch.float32, device="cuda")
-    pos = torch.zeros(st.q.shape[0], dtype=torch.int32, device="cuda")
-    with pytest.raises(pa.PaError) as e:
-        pa.pa_rope_write_kv(st.k_cache, st.v_cache, st.q, st.k_new, st.v_new, st.slot_mapping,
-                            pos, cos_sin, 128)
-    assert e.value.status == -4
+    out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                       st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
+                       workspace="auto" if path == "shares" else None, **s.kw())
+    torch.cuda.synchronize()
+    want, _ = oracle.paged_varlen(s.q, s.k, s.v, lay.cu_seqlens_q, lay.seq_lens,
+                                  lay.block_table, lay.scale, lay.block_size, "bf16",
+                                  kv_dtype="e4m3", k_scale=s.ks, v_scale=s.vs)
+    check_close(gpu_rows(out, "bf16"), want, "bf16",
+                groups=request_groups(lay, range(lay.num_seqs)),
+                label=f"{lay.name} e4m3 prefill {path}")
+
+
+def _bf16_rne(x32: np.ndarray) -> np.ndarray:
+    """fp32 values -> bf16 bits, round to nearest even."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("case", [(128, 32, 8, 128, True), (64, 8, 2, 32, False),
+                                  (128, 16, 4, 40, True)], ids=lambda c: "-".join(map(str, c)))
+def test_fp8_rope_write_kv(gpu_lib, case):
+    """RoPE + write on an E4M3 cache. q is rotated as for bf16 (within the
+    bf16 bound of the fp64 oracle). A rotated K element is the fp32 rotation
+    rounded to bf16, then quantised: its code must be one the fp64 value
+    allows, i.e. lie between the codes of the bf16 roundings of the value
+    plus and minus the fp32 rounding bound 2^-22 (|a| + |b|) (one code except
+    near a rounding boundary). V and the dimensions past rotary_dim are
+    quantised exactly as pa_write_kv does (bit for bit); tokens outside the
+    table, padding slots and every other slot are left alone."""
+    from oracle.rope import pair_index, rope_write_kv
+    d, hq, hkv, rdim, neox = case
+    t, nb, bs, maxpos = 60, 10, 16, 200
+    ks, vs = 0.05, 0.03
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    q = (torch.randn((t, hq, d), generator=gen, device="cuda") * 3).to(torch.bfloat16)
+    k_new = (torch.randn((t, hkv, d), generator=gen, device="cuda") * 3).to(torch.bfloat16)
+    v_new = torch.randn((t, hkv, d), generator=gen, device="cuda").to(torch.bfloat16)
+    kc = torch.full((nb, bs, hkv, d), 0x55, dtype=torch.uint8, device="cuda")
+    vc = torch.full_like(kc, 0x55)
+    rng = np.random.Generator(np.random.PCG64(78))
+    angles = rng.uniform(-50, 50, size=(maxpos, rdim // 2))
+    cos_sin = np.concatenate([np.cos(angles), np.sin(angles)], axis=1).astype(np.float32)
+    positions = rng.integers(0, maxpos, t).astype(np.int32)
+    positions[[2, 30]] = [-3, maxpos]                       # outside the table
+    slots = rng.permutation(nb * bs)[:t].astype(np.int64)
+    slots[[4, 31]] = -1                                     # padding tokens
+    q0, k0, v0 = raw_bits(q, "bf16"), raw_bits(k_new, "bf16"), raw_bits(v_new, "bf16")
+    pa.pa_rope_write_kv(kc.view(torch.float8_e4m3fn), vc.view(torch.float8_e4m3fn), q, k_new,
+                        v_new, torch.from_numpy(slots).cuda(),
+                        torch.from_numpy(positions).cuda(), torch.from_numpy(cos_sin).cuda(),
+                        rdim, neox, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    k_rot_cache = np.zeros((nb, bs, hkv, d))
+    v_dummy = np.zeros((nb, bs, hkv, d), dtype=np.uint16)
+    q_rot, k_rot = rope_write_kv(q0, k0, v0, slots, positions, cos_sin.astype(np.float64),
+                                 rdim, neox, "bf16", k_rot_cache, v_dummy, bs)
+    ok = (positions >= 0) & (positions < maxpos)
+    # q as in the bf16 path
+    first, second = pair_index(rdim, neox)
+    qw = oracle.widen(q0, "bf16")
+    qb = np.zeros_like(qw)
+    qs = np.abs(qw[..., first]) + np.abs(qw[..., second])
+    qb[..., first] = qb[..., second] = (2.0 ** -8 + 2.0 ** -22) * qs
+    q_got = oracle.widen(raw_bits(q, "bf16"), "bf16")
+    assert np.all(np.abs(q_got[ok] - q_rot[ok]) <= qb[ok])
+    assert np.array_equal(raw_bits(q, "bf16")[~ok], q0[~ok])
+    # K and V codes
+    kw = oracle.widen(k0, "bf16")
+    eps = np.zeros_like(kw)
+    es = np.abs(kw[..., first]) + np.abs(kw[..., second])
+    eps[..., first] = eps[..., second] = 2.0 ** -22 * es
+    kg = kc.cpu().numpy().reshape(nb * bs, hkv, d)
+    vg = vc.cpu().numpy().reshape(nb * bs, hkv, d)
+    written = np.zeros(nb * bs, bool)
+    for i in range(t):
+        if slots[i] < 0 or not ok[i]:
+            continue
+        written[slots[i]] = True
+        lo = np.nextafter((k_rot[i] - eps[i]).astype(np.float32), np.float32(-np.inf))
+        hi = np.nextafter((k_rot[i] + eps[i]).astype(np.float32), np.float32(np.inf))
+        c_lo = fp8.decode(fp8.quantize_bf16(_bf16_rne(lo), ks))
+        c_hi = fp8.decode(fp8.quantize_bf16(_bf16_rne(hi), ks))
+        got = fp8.decode(kg[slots[i]])
+        assert np.all((got >= c_lo) & (got <= c_hi)), f"token {i}: K code outside the allowed"
+        # pass-through dims and V: exactly the write's quantisation
+        assert np.array_equal(kg[slots[i]][..., rdim:], fp8.quantize_bf16(k0[i], ks)[..., rdim:])
+        assert np.array_equal(vg[slots[i]], fp8.quantize_bf16(v0[i], vs)), f"token {i}: V"
+    assert np.all(kg[~written] == 0x55) and np.all(vg[~written] == 0x55)
+    print(f"e4m3 rope {case}: {int(written.sum())} rows written", flush=True)
 
 
 def test_fp8_copy_blocks_bit_exact(gpu_lib):

@@ -117,8 +117,9 @@ def test_balanced_validation_codes(lib):
 
 
 def test_e4m3_cache_validation(lib):
-    """An E4M3 cache (dtype 3) needs finite positive scales; its prefill
-    tiles, the fused RoPE write and an E4M3 merge output are not offered."""
+    """An E4M3 cache (dtype 3) needs finite positive scales (checked before
+    anything else, prefill chunks and the fused RoPE write included); an
+    E4M3 merge output is not offered."""
     byref = ctypes.byref
     one = ctypes.c_void_p(1)
     for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("nan"), 1.0), (1.0, float("inf"))):
@@ -130,11 +131,12 @@ def test_e4m3_cache_validation(lib):
                          4, 64, 0.1, None) == 0
     c = _cache(dtype=3, ks=0.05, vs=0.02)
     assert lib.pa_decode(byref(c), None, None, None, None, 0, 8, 4, 64, 0.1, None) == 0
+    bad = _cache(dtype=3, ks=0.0, vs=0.02)
     # 40 query rows x group 4 > one 16-row tile: a prefill chunk
-    assert lib.pa_varlen(byref(c), one, one, one, one, one, 1, 40, 8, 4, 40, 64, 0.1, 1,
-                         None, 0, None) == -4
-    assert lib.pa_rope_write_kv(byref(c), one, 8, one, one, one, one, one, 128, 128, 1, 4,
-                                None) == -4
+    assert lib.pa_varlen(byref(bad), one, one, one, one, one, 1, 40, 8, 4, 40, 64, 0.1, 1,
+                         None, 0, None) == -2
+    assert lib.pa_rope_write_kv(byref(bad), one, 8, one, one, one, one, one, 128, 128, 1, 4,
+                                None) == -2
     assert lib.pa_lse_merge(one, None, one, one, one, 1, 8, 128, 64, 32, 3, None) == -3
 
 
