@@ -156,6 +156,101 @@ __global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const At
 
 }
 
+// Split-K partials (and whole-request decode, one split) with the KV heads
+// of a group read together: one workgroup per (request, group of NW KV
+// heads, split), one wave per head, the waves walking the split's blocks
+// side by side and meeting at a barrier every DEPTH blocks. One head's slice
+// of a block is a piece of each token row, so the workgroup fetches every
+// block whole, at once; one workgroup per head instead reads the slices of a
+// block at unrelated times. A wave's 16 rows are its head's GQA group (the
+// query rows of one token: decode rows only, no cu_seqlens). Writes the
+// split's normalised output and natural-log LSE, or with o_part == nullptr
+// the output rows.
+#ifndef PA_COAL_OCC
+#define PA_COAL_OCC 2
+#endif
+template <class E, int D, int NW>
+__global__ __launch_bounds__(NW * kWave, PA_COAL_OCC) void coalesced_attention_kernel(const AttnArgs a) {
+  using O = Ops<E, D>;
+  using S = typename O::storage;
+  using KS = typename O::kv_storage;
+  constexpr int kDepth = sizeof(KS) == 4 ? 1 : 2;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  int u = blockIdx.x;
+  const int split = u % a.num_splits;
+  u /= a.num_splits;
+  const int groups = a.num_kv_heads / NW;
+  const int hg = u % groups;
+  const int r = u / groups;
+  const int kvh = hg * NW + wave;
+  const int seq_len = min(max(a.seq_lens[r], 0), a.max_blocks * kBlockTokens);
+  const int g = a.group;
+  const int row = lane & 15, grp = lane >> 4;
+  const bool valid = row < g;
+  const int head = kvh * g + (valid ? row : 0);
+
+  KvView<KS> view;
+  view.k = static_cast<const KS*>(a.k_cache) + (int64_t)kvh * D;
+  view.v = static_cast<const KS*>(a.v_cache) + (int64_t)kvh * D;
+  view.rs = (int64_t)a.num_kv_heads * D;
+  view.table = a.block_table + (int64_t)r * a.max_blocks;
+  view.num_blocks = a.num_blocks;
+
+  typename O::Q qop;
+  O::load_q(qop, static_cast<const S*>(a.q) + ((int64_t)r * a.num_heads + head) * D, valid, lane);
+  const int nblk = (seq_len + kBlockTokens - 1) / kBlockTokens;
+  const int b0 = __builtin_amdgcn_readfirstlane(split * a.split_blocks);
+  const int n = __builtin_amdgcn_readfirstlane(max(min(a.split_blocks, nblk - b0), 0));
+  RowState<D> st;
+  st.init();
+  // every wave of the workgroup walks the same n blocks: same trip count
+  stream_blocks<E, D, kDepth, true>(st, qop, view, b0, n, valid ? seq_len : 0, seq_len,
+                                    a.scale_log2, lane);
+  st.l = sum_xor16(st.l);
+  st.l = sum_xor32(st.l);
+  if (!valid) return;
+  const float inv = (st.l > 0.f ? 1.f / st.l : 0.f) * a.out_scale;
+  const int64_t unit = (int64_t)r * a.num_heads + head;
+  if (a.o_part == nullptr) {
+    S* dst = static_cast<S*>(a.out) + unit * D + (D / 4) * grp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[D / 16];
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) v[c] = st.o[c][i] * inv;
+      store_chunk<E, D>(dst + (D / 16) * i, v);
+    }
+    return;
+  }
+  float* dst = a.o_part + (unit * a.num_splits + split) * D + (D / 4) * grp;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < D / 16; c += 4)
+      *reinterpret_cast<f32x4*>(dst + (D / 16) * i + c) =
+          f32x4{st.o[c][i] * inv, st.o[c + 1][i] * inv, st.o[c + 2][i] * inv,
+                st.o[c + 3][i] * inv};
+  if (grp == 0)
+    a.lse_part[unit * a.num_splits + split] =
+        st.l > 0.f ? (st.m + fast_log2(st.l)) * kLn2 : neg_inf();
+}
+
+template <class E, int D>
+hipError_t launch_coalesced_d(const AttnArgs& a, int nw, int64_t grid, hipStream_t stream) {
+  switch (nw) {
+    case 8:
+      coalesced_attention_kernel<E, D, 8><<<dim3((unsigned)grid), dim3(8 * kWave), 0, stream>>>(a);
+      break;
+    case 4:
+      coalesced_attention_kernel<E, D, 4><<<dim3((unsigned)grid), dim3(4 * kWave), 0, stream>>>(a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <class E, int D>
 hipError_t launch_dw(const AttnArgs& a, int waves, int64_t grid, hipStream_t stream) {
   switch (waves) {
@@ -183,6 +278,19 @@ hipError_t launch_d(const AttnArgs& a, int head_dim, int waves, int64_t grid,
 }
 
 }  // namespace
+
+hipError_t launch_coalesced(const AttnArgs& a, pa_dtype dtype, int head_dim, int nw,
+                            int64_t grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  const bool d128 = head_dim == 128;
+  switch (dtype) {
+    case PA_BF16: return d128 ? launch_coalesced_d<Bf16, 128>(a, nw, grid, stream) : launch_coalesced_d<Bf16, 64>(a, nw, grid, stream);
+    case PA_F16: return d128 ? launch_coalesced_d<F16, 128>(a, nw, grid, stream) : launch_coalesced_d<F16, 64>(a, nw, grid, stream);
+    case PA_F32: return d128 ? launch_coalesced_d<F32, 128>(a, nw, grid, stream) : launch_coalesced_d<F32, 64>(a, nw, grid, stream);
+    case PA_FP8_E4M3: return d128 ? launch_coalesced_d<Fp8, 128>(a, nw, grid, stream) : launch_coalesced_d<Fp8, 64>(a, nw, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_attention(const AttnArgs& args, pa_dtype dtype, int head_dim, int waves,
                             int64_t grid, hipStream_t stream) {

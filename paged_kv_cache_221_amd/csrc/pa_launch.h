@@ -124,6 +124,10 @@ hipError_t launch_write_kv(const pa_kv_cache* cache, const void* k_new, const vo
                            const int64_t* slot_mapping, int num_tokens, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& args, pa_dtype dtype, int head_dim, int waves,
                             int64_t grid, hipStream_t stream);
+// Decode rows (no cu_seqlens) with the KV heads of a group of nw (8 or 4)
+// read together: `grid` = B * (Hkv / nw) * num_splits workgroups of nw waves.
+hipError_t launch_coalesced(const AttnArgs& args, pa_dtype dtype, int head_dim, int nw,
+                            int64_t grid, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& args, pa_dtype out_dtype, hipStream_t stream);
 // Query tokens one prefill workgroup covers for GQA group size `group`.
 int prefill_tile_tokens(pa_dtype dtype, int group);

@@ -406,3 +406,77 @@ def test_varlen_long_prefill_tiles(gpu_lib, case, path):
     want, _ = varlen_oracle(st, snap, req)
     check_close(gpu_rows(out, dtype), want, dtype, groups=request_groups(lay, req),
                 label=f"{lay.name} {path}: long prefill")
+
+
+# ------------------------------------------------- head-coalesced kernel
+COALESCED_CASES = [("bf16", 128, 32, 8), ("f16", 64, 16, 4), ("f32", 128, 16, 8),
+                   ("e4m3", 128, 32, 8), ("bf16", 64, 32, 32)]
+
+
+@pytest.mark.parametrize("path", ["splitk", "decode"])
+@pytest.mark.parametrize("case", COALESCED_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_coalesced_decode_and_splitk(gpu_lib, case, path):
+    """Batches with at least four (request, KV-head group, split) units per
+    CU take the head-coalesced kernel (one workgroup per unit, one wave per
+    KV head of a group of 4 or 8): ragged lengths 0..1300 with 128-token
+    splits (many empty ones) for split-K + merge, and 1,100 requests (or 300
+    with 32 KV heads) for whole-request decode; every request checked."""
+    dtype, d, hq, hkv = case
+    cdt = "bf16" if dtype == "e4m3" else dtype
+    split = 128
+    rng = np.random.Generator(np.random.PCG64(4000 + d + hq + hkv))
+    if path == "splitk":
+        lens = rng.integers(1, 1300, size=170)
+    else:
+        lens = rng.integers(1, 300, size=1100 if hkv < 32 else 300)
+    lens[:3] = [5, 1, 16]       # request 0 is given seq_len 0 below
+    lay = build_layout(f"coalesced-{path}", cdt, lens.tolist(), [1] * len(lens), num_heads=hq,
+                       num_kv_heads=hkv, head_dim=d, block_size=16, seed=4001 + d,
+                       pool_factor=1.1)
+    kw = {}
+    if dtype == "e4m3":
+        from oracle import fp8
+        from workloads.tensors import materialize_e4m3
+        kw = dict(k_scale=0.0625, v_scale=0.05)
+        st = materialize_e4m3(lay, "cuda", kw["k_scale"], kw["v_scale"])
+        k_host, v_host = raw_bits(st.k_cache, "e4m3").copy(), raw_bits(st.v_cache, "e4m3").copy()
+        pa.pa_write_kv(st.k_cache, st.v_cache, st.k_new, st.v_new, st.slot_mapping, **kw)
+        fp8.write_kv(k_host, v_host, raw_bits(st.k_new, "bf16"), raw_bits(st.v_new, "bf16"),
+                     lay.slot_mapping, lay.block_size, kw["k_scale"], kw["v_scale"])
+        extra = dict(kv_dtype="e4m3", **kw)
+        q_host = raw_bits(st.q, "bf16")
+    else:
+        st, snap, _ = prepare(lay)
+        gpu_write(st)
+        snap.apply_oracle_write(lay)
+        k_host, v_host, q_host, extra = snap.k, snap.v, snap.q, {}
+    # request 0 attends to nothing (its new row is still written)
+    st.seq_lens[0] = 0
+    lens0 = lay.seq_lens.copy()
+    lens0[0] = 0
+    units = lay.num_seqs * (hkv // min(8, hkv)) * (-(-lay.max_seq_len // split)
+                                                    if path == "splitk" else 1)
+    assert units >= 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    if path == "splitk":
+        o, l = pa.pa_decode_splitk(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                                   lay.max_seq_len, split, lay.scale, **kw)
+        out, lse = pa.pa_lse_merge(o, l, st.seq_lens, lay.max_seq_len, split,
+                                   out_dtype=st.q.dtype, want_lse=True)
+    else:
+        out = pa.pa_decode(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                           lay.max_seq_len, lay.scale, **kw)
+    torch.cuda.synchronize()
+    want, want_lse = oracle.paged_decode(q_host, k_host, v_host, lay.block_table, lens0,
+                                         lay.scale, lay.block_size, cdt, **extra)
+    check_close(gpu_rows(out, cdt), want, cdt, label=f"{lay.name} {dtype} {d}/{hq}/{hkv}")
+    assert torch.all(out[0] == 0)                       # the empty request
+    if path == "splitk":
+        got_lse = lse.cpu().double().numpy()
+        assert np.array_equal(np.isneginf(got_lse), np.isneginf(want_lse))
+        fin = np.isfinite(want_lse)
+        assert max_err(got_lse[fin], want_lse[fin]) <= TOL[cdt]
+        # every split past a request's last one: exactly -inf and 0
+        nsplit = -(-lens0 // split)
+        lp = l.cpu().numpy()
+        for r in range(lay.num_seqs):
+            assert np.all(np.isneginf(lp[r, :, nsplit[r]:]))
