@@ -314,11 +314,354 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
   }
 }
 
+// ------------------------------------------------------------ 32-row tiles
+// 16-bit caches take 32 query rows per wave and a pair of blocks (32 keys)
+// per step on 32x32x16 MFMAs. S^T = K.Q^T leaves each lane 16 scores of one
+// query row -- register 4J + I holds key 8J + 4h + I of the pair, h being the
+// lane's half of the wave -- so a row's maximum is 15 in-lane maxima and one
+// exchange between the halves. P stays in its lane as the B operand of
+// O^T += V^T.P^T, one product per block and 32-dim chunk: contraction slot
+// 8h + 4J' + I of block b is key 8J' + 4h + I, i.e. registers 8b .. 8b + 7.
+// The matching A operand is V at keys {4h + I} and {8 + 4h + I} of the
+// block, one dim per lane row: V is staged in LDS transposed by key quads
+// (entry (quad, dim) = that dim of four consecutive keys, 8 bytes), so each
+// operand is two entries read as they are, with no permutes. Output rows are
+// dims (D/32)(8J + 4h + I) + c of chunk c, so each lane stores 4D/32
+// consecutive dims per J.
+template <class E>
+constexpr bool pf32() {
+  return sizeof(typename E::kv_storage) == 2 && sizeof(typename E::storage) == 2;
+}
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+template <class E>
+__device__ inline f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (std::is_same<E, Bf16>::value)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <int D>
+struct T32 {
+  static constexpr int kQc = D / 16;                          // QK products per pair
+  static constexpr int kOc = D / 32;                          // 32-dim output chunks
+  static constexpr int kKRow = 2 * D + 16;                    // padded K row in LDS (bytes)
+  static constexpr int kKPieces = kBlockTokens * (2 * D / 16);  // 16-byte K pieces per block
+  static constexpr int kVItems = 4 * (D / 2);                 // (key quad, dim pair) items per block
+  static constexpr int kVQuad = 8 * D;                        // bytes of one key quad in LDS
+  // LDS slot of dim entry e inside a quad. An operand read takes entry
+  // kOc * dslot + c in lane dslot (0..31): unswizzled, lanes 8 (D = 128) or 16
+  // (D = 64) apart would hit the same banks, so the entry index within each
+  // run of kOc is XORed with dslot / (32 / kOc), and 32 lanes' 8-byte reads
+  // cover all 64 banks.
+  __device__ static int vpos(int e) { return e ^ ((e >> 5) & (kOc - 1)); }
+};
+static_assert(kPrefillWaves * kWave >= T32<128>::kKPieces && kPrefillWaves * kWave >= T32<128>::kVItems,
+              "one staging item per thread and block");
+template <int D>
+struct PfLds32 {
+  char k[2][2][kBlockTokens * T32<D>::kKRow];  // [pair buffer][block][key row]
+  char v[2][2][4 * T32<D>::kVQuad];            // [pair buffer][block][quad][dim][4 keys]
+};
+// One block's staging registers of a thread: a 16-byte K piece, and one dword
+// (two dims) of each of the four keys of a V quad.
+struct Regs32 {
+  u32x4 k;
+  u32x4 v;
+};
+
+// As pf_piece, for 16-bit caches with 32 rows per wave (partial rows in tile
+// order: wave * 32 + row).
+template <class E, int D, int RING>
+__device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRequest& rq, int r,
+                                  int kvh, int tile, int b0, int b1, int64_t slot) {
+  using T = T32<D>;
+  using S = typename E::storage;
+  using KS = typename E::kv_storage;
+  static_assert(RING % 4 == 0, "pairs alternate between two LDS pair buffers");
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = a.group;
+  const int tpw = 32 / g;  // query tokens per wave
+  const int tok_base = tile * (kPrefillWaves * tpw);
+  const int n = rq.n, seq_len = rq.seq_len, ctx = rq.ctx, q_lo = rq.q_lo;
+  const int j = lane & 31, h = lane >> 5;  // the lane's query row (and key row, dim slot) and half
+
+  // the lane's query row: token tok, head hh of the GQA group
+  const int tok = tok_base + wave * tpw + j / g, hh = j - (j / g) * g;
+  const bool valid = j < tpw * g && tok < n;
+  const int key_end = !valid ? 0 : (a.causal ? min(ctx + tok + 1, seq_len) : seq_len);
+  u32x4 q[T::kQc];
+  {
+    const S* qrow = static_cast<const S*>(a.q) +
+                    ((int64_t)(q_lo + (valid ? tok : 0)) * a.num_heads + kvh * g + hh) * D;
+#pragma unroll
+    for (int c = 0; c < T::kQc; ++c)
+      q[c] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+  }
+  // a negative softmax scale is applied as a positive one to -q (exact)
+  const bool neg = a.scale_log2 < 0.f;
+  const float scale_log2 = neg ? -a.scale_log2 : a.scale_log2;
+  if (neg) {
+#pragma unroll
+    for (int c = 0; c < T::kQc; ++c) q[c] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
+
+  float m = neg_inf(), l = 0.f;
+  f32x16 o[T::kOc];
+#pragma unroll
+  for (int c = 0; c < T::kOc; ++c) o[c] = f32x16{};
+
+  // keys at or past b1 * 16 belong to the next piece; blocks before b_full
+  // are visible whole to every valid row of the wave (no mask)
+  const int kend = min(key_end, b1 * kBlockTokens);
+  int kmin = valid ? kend : 0x7fffffff;
+#pragma unroll
+  for (int s = 1; s < kWave; s <<= 1) kmin = min(kmin, __shfl_xor(kmin, s, kWave));
+  const int b_full = __builtin_amdgcn_readfirstlane(min(b1, kmin / kBlockTokens));
+
+  // staging: HBM -> registers (ring of RING blocks) -> LDS (two pair buffers)
+  const int64_t rs = (int64_t)a.num_kv_heads * D;
+  const int64_t block_elems = (int64_t)kBlockTokens * rs;
+  const int row_bytes_g = (int)(rs * (int64_t)sizeof(KS));
+  const KS* k_head = static_cast<const KS*>(a.k_cache) + (int64_t)kvh * D;
+  const KS* v_head = static_cast<const KS*>(a.v_cache) + (int64_t)kvh * D;
+  const __attribute__((address_space(4))) int32_t* tab =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)r * a.max_blocks);
+  constexpr int kPiecesPerRow = 2 * D / 16;
+  // a thread without an item reads past every range: zeros, no memory access
+  const int k_goff = tid < T::kKPieces
+                         ? (tid / kPiecesPerRow) * row_bytes_g + (tid % kPiecesPerRow) * 16
+                         : 0x40000000;
+  const int k_loff = (tid / kPiecesPerRow) * T::kKRow + (tid % kPiecesPerRow) * 16;
+  const int vq = tid / (D / 2), vdp = tid % (D / 2);
+  const int v_goff = tid < T::kVItems ? 4 * vq * row_bytes_g + 4 * vdp : 0x40000000;
+  // entries 2vdp and 2vdp + 1 land in one aligned 16-byte slot, swapped when
+  // the swizzle flips bit 0
+  const int v_loff = vq * T::kVQuad + 8 * (T::vpos(2 * vdp) & ~1);
+  const bool v_swap = (T::vpos(2 * vdp) & 1) != 0;
+  // Block ids of the loop's loads are read one group ahead by a vector load
+  // (lane k: block first + k) and taken from their lanes when used: scalar
+  // loads would share the LDS reads' wait counter, and every wait for an LDS
+  // result would then wait for them too.
+  const __attribute__((address_space(1))) int32_t* tabv =
+      (const __attribute__((address_space(1))) int32_t*)(a.block_table + (int64_t)r * a.max_blocks);
+  auto load_ids = [&](int first) { return tabv[min(first + (lane & (RING - 1)), b1 - 1)]; };
+  auto issue = [&](Regs32& rg, int i, int pb) {
+    const bool ok = i < b1 && pb >= 0 && pb < a.num_blocks;
+    const int keys = min(seq_len - i * kBlockTokens, kBlockTokens);
+    const int range = ok ? keys * row_bytes_g : 0;
+    const int64_t base = (int64_t)(ok ? pb : 0) * block_elems;
+    const Rsrc rk = make_rsrc(k_head + base, range), rv = make_rsrc(v_head + base, range);
+    rg.k = buf_load16<kPfAux>(rk, k_goff);
+    rg.v.x = buf_load4<kPfAux>(rv, v_goff);
+    rg.v.y = buf_load4<kPfAux>(rv, v_goff + row_bytes_g);
+    rg.v.z = buf_load4<kPfAux>(rv, v_goff + 2 * row_bytes_g);
+    rg.v.w = buf_load4<kPfAux>(rv, v_goff + 3 * row_bytes_g);
+  };
+  auto stage = [&](const Regs32& rg, int s, int bsel) {
+    if (tid < T::kKPieces) *reinterpret_cast<u32x4*>(&lds.k[s][bsel][k_loff]) = rg.k;
+    if (tid < T::kVItems) {
+      // keys 4vq .. 4vq + 3 of dims 2vdp (low halves) and 2vdp + 1 (high halves)
+      const u32x2 e0 = {__builtin_amdgcn_perm(rg.v.y, rg.v.x, 0x05040100u),
+                        __builtin_amdgcn_perm(rg.v.w, rg.v.z, 0x05040100u)};
+      const u32x2 e1 = {__builtin_amdgcn_perm(rg.v.y, rg.v.x, 0x07060302u),
+                        __builtin_amdgcn_perm(rg.v.w, rg.v.z, 0x07060302u)};
+      const u32x2 first = v_swap ? e1 : e0, second = v_swap ? e0 : e1;
+      *reinterpret_cast<u32x4*>(&lds.v[s][bsel][v_loff]) = u32x4{first.x, first.y, second.x, second.y};
+    }
+  };
+
+  // S^T of the pair in LDS pair buffer s (keys x rows, 32 x 32)
+  auto qk = [&](int s) {
+    const char* kb = &lds.k[s][j >> 4][(j & 15) * T::kKRow + 16 * h];
+    u32x4 kk[T::kQc];
+#pragma unroll
+    for (int c = 0; c < T::kQc; ++c) kk[c] = *reinterpret_cast<const u32x4*>(kb + 32 * c);
+    f32x16 acc = {};
+#pragma unroll
+    for (int c = 0; c < T::kQc; ++c) acc = mma32<E>(kk[c], q[c], acc);
+    return acc;
+  };
+  // online softmax of one pair's scores (keys key0 .. key0 + 31): the
+  // probabilities relative to the row's reference m, and the factor for o
+  // and l when m moves
+  auto softmax = [&](const f32x16& acc, int key0, float (&p)[16], auto masked) {
+    float alpha;
+    if constexpr (decltype(masked)::value) {
+      float sv[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int key = key0 + 8 * (t >> 2) + 4 * h + (t & 3);
+        sv[t] = key < kend ? acc[t] * scale_log2 : neg_inf();
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int t = 1; t < 16; ++t) mx = fmax2(mx, sv[t]);
+      mx = max_xor32(mx);
+      alpha = advance_max(m, mx);
+      const float m_use = m == neg_inf() ? 0.f : m;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) p[t] = fast_exp2(sv[t] - m_use);
+    } else {
+      // every key visible and scale_log2 >= 0: the scaled maximum of the raw
+      // scores is the maximum of the scaled ones, and each exponent is one
+      // fused multiply-add
+      float mx = acc[0];
+#pragma unroll
+      for (int t = 1; t < 16; ++t) mx = fmax2(mx, acc[t]);
+      mx = max_xor32(mx) * scale_log2;
+      alpha = advance_max(m, mx);
+      const float neg_m = -m;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(acc[t], scale_log2, neg_m));
+    }
+    return alpha;
+  };
+  // l and o take the pair: rescale when the reference moved, then P.V with
+  // the values from pair buffer s
+  auto accumulate = [&](const float (&p)[16], float alpha, int s) {
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; t += 4) ps += (p[t] + p[t + 1]) + (p[t + 2] + p[t + 3]);
+    l = l * alpha + ps;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int c = 0; c < T::kOc; ++c) o[c] *= alpha;
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const u32x4 pk = {E::pack2(p[8 * b], p[8 * b + 1]), E::pack2(p[8 * b + 2], p[8 * b + 3]),
+                        E::pack2(p[8 * b + 4], p[8 * b + 5]), E::pack2(p[8 * b + 6], p[8 * b + 7])};
+      const char* vb = &lds.v[s][b][0];
+#pragma unroll
+      for (int c = 0; c < T::kOc; ++c) {
+        const int e = 8 * T::vpos(T::kOc * j + c);
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vb + h * T::kVQuad + e);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vb + (h + 2) * T::kVQuad + e);
+        o[c] = mma32<E>(u32x4{lo.x, lo.y, hi.x, hi.y}, pk, o[c]);
+      }
+    }
+  };
+
+  int nid = load_ids(b0 + RING);  // lane k: the id of the block the group's load k reads
+  Regs32 ring[RING];
+#pragma unroll
+  for (int jj = 0; jj < RING; ++jj) issue(ring[jj], b0 + jj, tab[min(b0 + jj, b1 - 1)]);
+  // take the ids in here (a wait for the one load issued before the ring's):
+  // entering the loop with the load still pending makes the compiler wait
+  // for nearly every load at the top of each group
+  asm volatile("" ::"v"(nid));
+  // One group of RING blocks (RING / 2 pairs); the ring slot of block i is
+  // (i - b0) % RING. Blocks are consumed unconditionally, like the loads: a
+  // padding block at or past b1 was read as zeros and its keys are past
+  // every row's limit (kend), so it adds nothing.
+  auto group = [&](int i0, auto masked) {
+    const int nxt = load_ids(i0 + 2 * RING);
+#pragma unroll
+    for (int jj = 0; jj < RING; jj += 2) {
+      const int i = i0 + jj;
+      const int s = (jj >> 1) & 1;
+      stage(ring[jj], s, 0);
+      stage(ring[jj + 1], s, 1);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ring[jj], i + RING, __builtin_amdgcn_readlane(nid, jj));
+      issue(ring[jj + 1], i + 1 + RING, __builtin_amdgcn_readlane(nid, jj + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      float pr[16];
+      const float alpha = softmax(qk(s), i * kBlockTokens, pr, masked);
+      accumulate(pr, alpha, s);
+    }
+    nid = nxt;
+  };
+  int i0 = b0;
+  for (; i0 + RING <= b_full; i0 += RING) group(i0, std::false_type{});
+  for (; i0 < b1; i0 += RING) group(i0, std::true_type{});
+
+  // epilogue: normalise and store (partials when cut)
+  l = sum_xor32(l);
+  if (valid) {
+    const float inv = (l > 0.f ? 1.f / l : 0.f) * a.out_scale;
+    constexpr int kRun = 4 * T::kOc;  // consecutive dims per J
+    if (slot < 0) {
+      S* dst = static_cast<S*>(a.out) + ((int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh) * D;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        unsigned w[kRun / 2];
+#pragma unroll
+        for (int x = 0; x < kRun; x += 2) {
+          // value x of the run is dim slot 8J + 4h + x / kOc, chunk x % kOc
+          w[x / 2] = E::pack2(o[x % T::kOc][4 * J + x / T::kOc] * inv,
+                              o[(x + 1) % T::kOc][4 * J + (x + 1) / T::kOc] * inv);
+        }
+        S* d = dst + T::kOc * (8 * J + 4 * h);
+#pragma unroll
+        for (int x = 0; x < kRun / 2; x += 4)
+          *reinterpret_cast<u32x4*>(d + 2 * x) = u32x4{w[x], w[x + 1], w[x + 2], w[x + 3]};
+      }
+    } else {
+      const int64_t prow = slot * (kPrefillWaves * 32) + wave * 32 + j;
+      float* dst = a.pf_o + prow * D;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        float* d = dst + T::kOc * (8 * J + 4 * h);
+#pragma unroll
+        for (int x = 0; x < kRun; x += 4)
+          *reinterpret_cast<f32x4*>(d + x) =
+              f32x4{o[x % T::kOc][4 * J + x / T::kOc] * inv,
+                    o[(x + 1) % T::kOc][4 * J + (x + 1) / T::kOc] * inv,
+                    o[(x + 2) % T::kOc][4 * J + (x + 2) / T::kOc] * inv,
+                    o[(x + 3) % T::kOc][4 * J + (x + 3) / T::kOc] * inv};
+      }
+      if (h == 0) a.pf_lse[prow] = l > 0.f ? m + fast_log2(l) : neg_inf();
+    }
+  }
+}
+
+// fp32 operands are twice the size: half the row tiles and half the ring.
+template <class E>
+constexpr int prefill_rt() {
+  return sizeof(typename E::storage) == 4 ? (PA_PREFILL_RT + 1) / 2 : PA_PREFILL_RT;
+}
+template <class E>
+constexpr int prefill_ring() {
+  return sizeof(typename E::storage) == 4 ? PA_PREFILL_RING / 2 : PA_PREFILL_RING;
+}
+
+// Query rows per wave and query tokens per wave of the prefill tiles.
+template <class E>
+constexpr int pf_wave_rows() {
+  return pf32<E>() ? 32 : kTileRows * prefill_rt<E>();
+}
+// Rows of one unit of the row layout: a 32-row wave tile, or a 16-row tile.
+template <class E>
+constexpr int pf_unit_rows() {
+  return pf32<E>() ? 32 : kTileRows;
+}
+template <class E>
+__device__ __host__ inline int pf_wave_tokens(int g) {
+  return (pf_wave_rows<E>() / pf_unit_rows<E>()) * (pf_unit_rows<E>() / g);
+}
+template <class E, int D>
+using PfLdsOf = typename std::conditional<pf32<E>(), PfLds32<D>, PfLds<E, D>>::type;
+
+template <class E, int D, int RT, int RING>
+__device__ inline void pf_run_piece(const AttnArgs& a, PfLdsOf<E, D>& lds, const PfRequest& rq,
+                                    int r, int kvh, int tile, int b0, int b1, int64_t slot) {
+  if constexpr (pf32<E>())
+    pf_piece32<E, D, RING>(a, lds, rq, r, kvh, tile, b0, b1, slot);
+  else
+    pf_piece<E, D, RT, RING>(a, lds, rq, r, kvh, tile, b0, b1, slot);
+}
+
 // One workgroup per (tile, request, KV head), tiles in descending order (the
 // tiles that see the most keys start first); every tile written whole.
 template <class E, int D, int RT, int RING>
 __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) PfLds<E, D> lds;
+  __shared__ __attribute__((aligned(16))) PfLdsOf<E, D> lds;
   int u = blockIdx.x;
   const int kvh = u % a.num_kv_heads;
   u /= a.num_kv_heads;
@@ -326,11 +669,11 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_kerne
   const int tile = a.num_tiles - 1 - u / a.num_seqs;
   const PfRequest rq = pf_request(a, r);
   if (!pf_is_prefill(rq, a.group)) return;  // a single-tile request: the decode kernel's
-  const int tile_tokens = kPrefillWaves * RT * (kTileRows / a.group);
+  const int tile_tokens = kPrefillWaves * pf_wave_tokens<E>(a.group);
   if (tile * tile_tokens >= rq.n) return;
   const int nblk = pf_tile_blocks(a, rq, tile, tile_tokens);
   if (nblk <= 0) return;
-  pf_piece<E, D, RT, RING>(a, lds, rq, r, kvh, tile, 0, nblk, -1);
+  pf_run_piece<E, D, RT, RING>(a, lds, rq, r, kvh, tile, 0, nblk, -1);
 }
 
 // Exclusive prefix sum over the workgroup (int64); *total gets the sum.
@@ -371,14 +714,17 @@ __device__ inline int64_t pf_request_items(const AttnArgs& a, const PfRequest& r
 // Writes the merge record of every query token of a tile for one KV head:
 // first partial slot, piece count (0: the tile was written whole) and the
 // token's first row in the tile's partial slot.
+// Rows are laid out in units of `unit` rows (a 16-row tile, or a 32-row
+// wave tile), each holding unit / g whole tokens.
+template <int UNIT>
 __device__ inline void pf_write_records(const AttnArgs& a, const PfRequest& rq, int kvh,
                                         int tile, int tile_tokens, int s0, int cnt) {
-  const int g = a.group, tpw = kTileRows / g;
+  const int g = a.group, tpu = UNIT / g;
   const int t0 = tile * tile_tokens;
   const int nt = min(tile_tokens, rq.n - t0);
   for (int i = threadIdx.x; i < nt; i += kPrefillThreads)
     a.pf_rec[(int64_t)(rq.q_lo + t0 + i) * a.num_kv_heads + kvh] =
-        int4{s0, cnt, (i / tpw) * kTileRows + (i % tpw) * g, 0};
+        int4{s0, cnt, (i / tpu) * UNIT + (i % tpu) * g, 0};
 }
 
 // Equal shares: the W items -- (request, KV head, tile, KV block) in that
@@ -394,12 +740,12 @@ __device__ inline void pf_write_records(const AttnArgs& a, const PfRequest& rq, 
 // writes empty records for the batch's other tokens.
 template <class E, int D, int RT, int RING>
 __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_shares_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) PfLds<E, D> lds;
+  __shared__ __attribute__((aligned(16))) PfLdsOf<E, D> lds;
   __shared__ int64_t s_pre[kMaxBalancedSeqs + 1];
   __shared__ int64_t s_tmp[kPrefillWaves];
   const int tid = threadIdx.x;
   const int B = a.num_seqs, hkv = a.num_kv_heads, g = a.group;
-  const int tile_tokens = kPrefillWaves * RT * (kTileRows / g);
+  const int tile_tokens = kPrefillWaves * pf_wave_tokens<E>(g);
 
   // 1. items before each request, in LDS
   const int per = (B + kPrefillThreads - 1) / kPrefillThreads;
@@ -473,7 +819,7 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_share
       const int64_t slot = whole ? -1 : 2 * j + (x == lo ? 0 : 1);
       if (!first) __syncthreads();  // the previous piece's LDS reads are done
       first = false;
-      pf_piece<E, D, RT, RING>(a, lds, rq, r, kvh, tile, b0, b1, slot);
+      pf_run_piece<E, D, RT, RING>(a, lds, rq, r, kvh, tile, b0, b1, slot);
       int s0 = 0, cnt = 0;
       if (!whole) {
         // shares holding the tile's first and last KV block
@@ -482,7 +828,7 @@ __global__ __launch_bounds__(kPrefillThreads, PA_PREFILL_OCC) void prefill_share
         s0 = (int)(2 * j0 + (t_begin == begin_of(j0) ? 0 : 1));
         cnt = (int)(j1 - j0 + 1);
       }
-      pf_write_records(a, rq, kvh, tile, tile_tokens, s0, cnt);
+      pf_write_records<pf_unit_rows<E>()>(a, rq, kvh, tile, tile_tokens, s0, cnt);
     }
     x += len;
   }
@@ -580,16 +926,6 @@ __global__ __launch_bounds__(4 * kWave) void prefill_share_merge_kernel(const At
   }
 }
 
-// fp32 operands are twice the size: half the row tiles and half the ring.
-template <class E>
-constexpr int prefill_rt() {
-  return sizeof(typename E::storage) == 4 ? (PA_PREFILL_RT + 1) / 2 : PA_PREFILL_RT;
-}
-template <class E>
-constexpr int prefill_ring() {
-  return sizeof(typename E::storage) == 4 ? PA_PREFILL_RING / 2 : PA_PREFILL_RING;
-}
-
 template <class E, int D>
 hipError_t launch_pf(const AttnArgs& a, int64_t grid, hipStream_t stream) {
   prefill_kernel<E, D, prefill_rt<E>(), prefill_ring<E>()>
@@ -620,13 +956,19 @@ int resident_pf_shares() {
 }  // namespace
 
 int prefill_tile_tokens(pa_dtype dtype, int group) {
-  const int rt = dtype == PA_F32 ? prefill_rt<F32>() : prefill_rt<Bf16>();
-  return kPrefillWaves * rt * (kTileRows / group);
+  switch (dtype) {
+    case PA_F32: return kPrefillWaves * pf_wave_tokens<F32>(group);
+    case PA_FP8_E4M3: return kPrefillWaves * pf_wave_tokens<Fp8>(group);
+    default: return kPrefillWaves * pf_wave_tokens<Bf16>(group);
+  }
 }
 
 int prefill_rows(pa_dtype dtype) {
-  const int rt = dtype == PA_F32 ? prefill_rt<F32>() : prefill_rt<Bf16>();
-  return kPrefillWaves * rt * kTileRows;
+  switch (dtype) {
+    case PA_F32: return kPrefillWaves * pf_wave_rows<F32>();
+    case PA_FP8_E4M3: return kPrefillWaves * pf_wave_rows<Fp8>();
+    default: return kPrefillWaves * pf_wave_rows<Bf16>();
+  }
 }
 
 int prefill_resident_shares(pa_dtype dtype, int head_dim) {
