@@ -4,14 +4,15 @@
 // prefill chunk: query row i of it sees keys 0 .. c + i (its cached context c
 // plus itself and earlier new tokens [P1 §04 causal mask]). Prefill is a dense
 // contraction [P1 §04 table: GEMM, compute-bound], so the work is arranged for
-// operand reuse: a workgroup owns 4 waves x RT row tiles x 16/g query tokens
-// of one (request, KV head); every KV block is fetched once per workgroup into
+// operand reuse: a workgroup of 4 waves owns a tile of query tokens of one
+// (request, KV head); every KV block is fetched once per workgroup into
 // double-buffered LDS through a register prefetch ring of PA_PREFILL_RING
-// blocks, and each wave reads the block's MFMA operands from LDS once and
-// applies them to all of its RT row tiles. 16-bit operands are staged and
-// consumed two blocks at a time, so that P.V runs as full-rate 16x16x32
-// products. Scores and probabilities stay in registers (the FlashAttention
-// principle [P3 §3.4]).
+// blocks, and each wave reads the block's MFMA operands from LDS once for all
+// of its rows. bf16 and fp16 caches give each wave 32 rows and consume blocks
+// in pairs on 32x32x16 products (pf_piece32); E4M3 caches give it RT row
+// tiles of 16 rows and consume pairs on 16x16 products, fp32 caches one row
+// tile and single blocks (pf_piece). Scores and probabilities stay in
+// registers (the FlashAttention principle [P3 §3.4]).
 //
 // A workgroup's time is its tile's key count, which in a causal chunk grows
 // with the tile's position and with the request's cached context: one
