@@ -124,6 +124,7 @@ struct Bf16 {
     u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even
     return (uint16_t)(u >> 16);
   }
+  __device__ static float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
   __device__ static f32x4 mma_qk(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -146,6 +147,7 @@ struct F16 {
     _Float16 h = (_Float16)f;  // hardware conversion, round to nearest even
     return __builtin_bit_cast(uint16_t, h);
   }
+  __device__ static float to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
   __device__ static f32x4 mma_qk(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -746,6 +748,41 @@ __device__ inline void store_chunk(typename Ops<E, D>::storage* dst, const float
     for (int j = 0; j < n / 4; ++j)
       *reinterpret_cast<f32x4*>(dst + 4 * j) = f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2],
                                                     v[4 * j + 3]};
+  }
+}
+
+// Partial output rows -- the pieces of cut segments and tiles, merged by
+// their LSEs -- are kept in the output's storage type: the merged row is
+// rounded to that type anyway, and 16-bit partials halve the bytes written
+// and read back. Loads of n (4 or 8) consecutive partial values, widened.
+template <class E, int N>
+__device__ inline void load_part(const typename E::storage* p, float* v) {
+  static_assert(N == 4 || N == 8, "4 or 8 values");
+  if constexpr (sizeof(typename E::storage) == 2) {
+    if constexpr (N == 8) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = E::to_f32((uint16_t)(w[k] & 0xffffu));
+        v[2 * k + 1] = E::to_f32((uint16_t)(w[k] >> 16));
+      }
+    } else {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        v[2 * k] = E::to_f32((uint16_t)(w[k] & 0xffffu));
+        v[2 * k + 1] = E::to_f32((uint16_t)(w[k] >> 16));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; k += 4) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(p + k);
+      v[k] = w[0];
+      v[k + 1] = w[1];
+      v[k + 2] = w[2];
+      v[k + 3] = w[3];
+    }
   }
 }
 

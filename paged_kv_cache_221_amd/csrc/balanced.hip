@@ -318,14 +318,14 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
         }
       } else {
         const int64_t slot = ((int64_t)wave * head_slots + piece_slot(j, sg)) * a.slot_rows + row;
-        float* dst = a.part_o + slot * D + (D / 4) * grp;
+        S* dst = static_cast<S*>(a.part_o) + slot * D + (D / 4) * grp;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          float v[D / 16];
 #pragma unroll
-          for (int c = 0; c < D / 16; c += 4)
-            *reinterpret_cast<f32x4*>(dst + (D / 16) * i + c) =
-                f32x4{st.o[c][i] * inv, st.o[c + 1][i] * inv, st.o[c + 2][i] * inv,
-                      st.o[c + 3][i] * inv};
+          for (int c = 0; c < D / 16; ++c) v[c] = st.o[c][i] * inv;
+          store_chunk<E, D>(dst + (D / 16) * i, v);
+        }
         if (grp == 0) a.part_lse[slot] = st.l > 0.f ? st.m + fast_log2(st.l) : neg_inf();
       }
     }
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const Balance
   const int np = rec.y;
   if (np <= 0) return;  // written whole by one workgroup, or an empty request
   const int64_t sr = a.slot_rows;
-  const float* po = a.part_o + (int64_t)rec.x * sr * D;
+  const S* po = static_cast<const S*>(a.part_o) + (int64_t)rec.x * sr * D;
   const float* pl = a.part_lse + (int64_t)rec.x * sr;
   for (int f = lane * 8; f < n_r * g * D; f += kWave * 8) {
     const int row = f / D, dim = f - row * D;
@@ -394,15 +394,13 @@ __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const Balance
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     for (int k0 = 0; k0 < np; k0 += kMergeBatch) {
       float l[kMergeBatch];
-      f32x4 v[kMergeBatch][2];
+      float v[kMergeBatch][8];
 #pragma unroll
       for (int kk = 0; kk < kMergeBatch; ++kk) {
         // past the last piece: reload it (in bounds), weighted 0 below
         const int64_t k = min(k0 + kk, np - 1);
         l[kk] = pl[k * sr + row];
-        const f32x4* src = reinterpret_cast<const f32x4*>(po + k * sr * D + f);
-        v[kk][0] = src[0];
-        v[kk][1] = src[1];
+        load_part<E, 8>(po + k * sr * D + f, v[kk]);
       }
       float mb = m;
 #pragma unroll
@@ -418,10 +416,7 @@ __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const Balance
         const float w = k0 + kk < np ? fast_exp2(l[kk] - mu) : 0.f;
         wsum += w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] += w * v[kk][0][e];
-          acc[4 + e] += w * v[kk][1][e];
-        }
+        for (int e = 0; e < 8; ++e) acc[e] += w * v[kk][e];
       }
       m = mb;
     }

@@ -263,7 +263,7 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, const void* q, co
   a.out = out;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
-  a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+  a.part_o = static_cast<void*>(ws + lay.part_o);
   a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
   a.records = reinterpret_cast<int2*>(ws + lay.records);
   a.cu_seqlens = nullptr;
@@ -548,7 +548,7 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
     a.num_tiles = (max_query_len + tt - 1) / tt;
     if (use_ws && vl.pf_shares > 0) {
       a.pf_shares = vl.pf_shares;
-      a.pf_o = reinterpret_cast<float*>(ws + vl.pf_o);
+      a.pf_o = static_cast<void*>(ws + vl.pf_o);
       a.pf_lse = reinterpret_cast<float*>(ws + vl.pf_lse);
       a.pf_rec = reinterpret_cast<int4*>(ws + vl.pf_rec);
     }
@@ -572,7 +572,7 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
     b.block_table = block_table;
     b.seq_lens = seq_lens;
     b.cu_seqlens = cu_seqlens_q;
-    b.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+    b.part_o = static_cast<void*>(ws + lay.part_o);
     b.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
     b.records = reinterpret_cast<int2*>(ws + lay.records);
     b.num_tokens = num_tokens;

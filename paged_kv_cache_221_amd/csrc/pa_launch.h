@@ -36,7 +36,7 @@ struct AttnArgs {
   // an equal contiguous share of the batch's (request, KV head, tile, KV
   // block) items; pieces that cut a tile write partials here. With
   // pf_shares == 0, one workgroup per (tile, request, KV head), no partials.
-  float* pf_o;               // [2 * pf_shares, prefill_rows, D] normalised partial rows
+  void* pf_o;                // [2 * pf_shares, prefill_rows, D] normalised partial rows (output type)
   float* pf_lse;             // [2 * pf_shares, prefill_rows] partial LSEs (log2 domain)
   int4* pf_rec;              // [T, Hkv] per token: (first slot, pieces, row in slot, 0)
   int pf_shares;
@@ -83,7 +83,7 @@ struct BalancedArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* cu_seqlens;  // nullptr: one query token per request (decode)
-  float* part_o;              // [balanced_piece_slots, slot_rows, D] partial outputs
+  void* part_o;               // [balanced_piece_slots, slot_rows, D] partial outputs (output type)
   float* part_lse;            // [balanced_piece_slots, slot_rows] partial LSEs (log2 domain)
   int2* records;              // [B, Hkv] (first piece slot, piece count; 0 = no merge)
   int num_tokens;             // T (rows of q) when cu_seqlens is set

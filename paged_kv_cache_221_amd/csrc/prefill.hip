@@ -301,14 +301,14 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
       } else {
         const int64_t prow =
             slot * (kPrefillWaves * RT * kTileRows) + (wave * RT + rt) * kTileRows + row;
-        float* dst = a.pf_o + prow * D + (D / 4) * grp;
+        S* dst = static_cast<S*>(a.pf_o) + prow * D + (D / 4) * grp;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          float v[D / 16];
 #pragma unroll
-          for (int c = 0; c < D / 16; c += 4)
-            *reinterpret_cast<f32x4*>(dst + (D / 16) * i + c) =
-                f32x4{st[rt].o[c][i] * inv, st[rt].o[c + 1][i] * inv, st[rt].o[c + 2][i] * inv,
-                      st[rt].o[c + 3][i] * inv};
+          for (int c = 0; c < D / 16; ++c) v[c] = st[rt].o[c][i] * inv;
+          store_chunk<E, D>(dst + (D / 16) * i, v);
+        }
         if (grp == 0) a.pf_lse[prow] = st[rt].l > 0.f ? st[rt].m + fast_log2(st[rt].l) : neg_inf();
       }
     }
@@ -587,38 +587,25 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   if (valid) {
     const float inv = (l > 0.f ? 1.f / l : 0.f) * a.out_scale;
     constexpr int kRun = 4 * T::kOc;  // consecutive dims per J
-    if (slot < 0) {
-      S* dst = static_cast<S*>(a.out) + ((int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh) * D;
+    // the output row, or the piece's partial row (same type)
+    const int64_t prow = slot * (kPrefillWaves * 32) + wave * 32 + j;
+    S* dst = slot < 0 ? static_cast<S*>(a.out) + ((int64_t)(q_lo + tok) * a.num_heads + kvh * g + hh) * D
+                      : static_cast<S*>(a.pf_o) + prow * D;
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        unsigned w[kRun / 2];
+    for (int J = 0; J < 4; ++J) {
+      unsigned w[kRun / 2];
 #pragma unroll
-        for (int x = 0; x < kRun; x += 2) {
-          // value x of the run is dim slot 8J + 4h + x / kOc, chunk x % kOc
-          w[x / 2] = E::pack2(o[x % T::kOc][4 * J + x / T::kOc] * inv,
-                              o[(x + 1) % T::kOc][4 * J + (x + 1) / T::kOc] * inv);
-        }
-        S* d = dst + T::kOc * (8 * J + 4 * h);
-#pragma unroll
-        for (int x = 0; x < kRun / 2; x += 4)
-          *reinterpret_cast<u32x4*>(d + 2 * x) = u32x4{w[x], w[x + 1], w[x + 2], w[x + 3]};
+      for (int x = 0; x < kRun; x += 2) {
+        // value x of the run is dim slot 8J + 4h + x / kOc, chunk x % kOc
+        w[x / 2] = E::pack2(o[x % T::kOc][4 * J + x / T::kOc] * inv,
+                            o[(x + 1) % T::kOc][4 * J + (x + 1) / T::kOc] * inv);
       }
-    } else {
-      const int64_t prow = slot * (kPrefillWaves * 32) + wave * 32 + j;
-      float* dst = a.pf_o + prow * D;
+      S* d = dst + T::kOc * (8 * J + 4 * h);
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        float* d = dst + T::kOc * (8 * J + 4 * h);
-#pragma unroll
-        for (int x = 0; x < kRun; x += 4)
-          *reinterpret_cast<f32x4*>(d + x) =
-              f32x4{o[x % T::kOc][4 * J + x / T::kOc] * inv,
-                    o[(x + 1) % T::kOc][4 * J + (x + 1) / T::kOc] * inv,
-                    o[(x + 2) % T::kOc][4 * J + (x + 2) / T::kOc] * inv,
-                    o[(x + 3) % T::kOc][4 * J + (x + 3) / T::kOc] * inv};
-      }
-      if (h == 0) a.pf_lse[prow] = l > 0.f ? m + fast_log2(l) : neg_inf();
+      for (int x = 0; x < kRun / 2; x += 4)
+        *reinterpret_cast<u32x4*>(d + 2 * x) = u32x4{w[x], w[x + 1], w[x + 2], w[x + 3]};
     }
+    if (slot >= 0 && h == 0) a.pf_lse[prow] = l > 0.f ? m + fast_log2(l) : neg_inf();
   }
 }
 
@@ -848,6 +835,7 @@ constexpr int kPieceBatch = 4;
 template <class E, int DPL>
 __global__ __launch_bounds__(4 * kWave) void prefill_share_merge_kernel(const AttnArgs a,
                                                                         int pf_rows, int D) {
+  using S = typename E::storage;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
   if (unit >= (int64_t)a.num_tokens * a.num_kv_heads) return;
@@ -874,15 +862,17 @@ __global__ __launch_bounds__(4 * kWave) void prefill_share_merge_kernel(const At
       const bool ok = p < cnt;
       const int64_t sr = (p == 0 ? s0 : 2 * ((int64_t)(s0 >> 1) + p)) * pf_rows + prow;
       lse[k] = ok ? a.pf_lse[sr] : neg_inf();
-      const float* o = a.pf_o + (ok ? sr : 0) * D + d0;
+      // a piece past cnt reads slot 0 (in bounds; any bits) and counts as zeros
+      const S* o = static_cast<const S*>(a.pf_o) + (ok ? sr : 0) * D + d0;
 #pragma unroll
-      for (int i = 0; i < DPL; i += 4) {
-        const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(o + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-        v[k][i] = x[0];
-        v[k][i + 1] = x[1];
-        v[k][i + 2] = x[2];
-        v[k][i + 3] = x[3];
+      for (int i = 0; i < DPL; i += 8) {
+        if constexpr (DPL >= 8)
+          load_part<E, 8>(o + i, &v[k][i]);
+        else
+          load_part<E, 4>(o + i, &v[k][i]);
       }
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) v[k][i] = ok ? v[k][i] : 0.f;
     }
     float mn = m;
 #pragma unroll
@@ -902,7 +892,6 @@ __global__ __launch_bounds__(4 * kWave) void prefill_share_merge_kernel(const At
     m = mn;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  using S = typename E::storage;
   const int token = (int)(unit / a.num_kv_heads), kvh = (int)(unit - (int64_t)token * a.num_kv_heads);
   S* out = static_cast<S*>(a.out) + ((int64_t)token * a.num_heads + kvh * g + hh) * D + d0;
   // the lane's DPL consecutive outputs in 8- or 16-byte stores
