@@ -167,10 +167,11 @@ pa_status pa_lse_merge(void *out, float *lse_out, const float *o_part,
  * do not leave the GPU idle while the longest ones finish; the waves of a
  * workgroup (one per KV head of the group) read each block together. A
  * share's end that cuts a (request, KV head) is written as a partial
- * (softmax-normalised output and log-sum-exp) and a second kernel
- * renormalises the partials, as the Flash-Decoding merge of [P1 §07] does,
- * with split points chosen for balance. Two kernels are launched on
- * `stream`.
+ * (softmax-normalised output, rounded to the output's type, and its fp32
+ * log-sum-exp) and a second kernel renormalises the partials, as the
+ * Flash-Decoding merge of [P1 §07] does, with split points chosen for
+ * balance; a cut row is thus rounded to a 16-bit output type twice. Two
+ * kernels are launched on `stream`.
  *   workspace       : caller-owned device memory of at least
  *                     pa_decode_balanced_workspace_bytes(...) bytes; its
  *                     contents need not be initialised; two calls in flight
@@ -241,8 +242,9 @@ pa_status pa_write_decode_balanced_noalloc(const pa_kv_cache *cache, void *out, 
  * given (partials merged by a further kernel), else one workgroup per
  * (request, KV head). With a workspace, the prefill tiles' KV blocks are also
  * cut into one equal share per resident workgroup, and the tiles cut between
- * shares are renormalised by a merge kernel [P1 §07]; without one, each
- * (tile, request, KV head) gets its own workgroup.
+ * shares are renormalised by a merge kernel [P1 §07] (partials kept in the
+ * output's type, as in pa_decode_balanced); without one, each (tile,
+ * request, KV head) gets its own workgroup.
  *   out, q        : [T, Hq, D] in cache->dtype
  *   cu_seqlens_q  : int32 [B + 1], cu[0] = 0, non-decreasing, cu[B] = T
  *   seq_lens      : int32 [B]; KV length including this step's n_r tokens
