@@ -352,11 +352,13 @@ struct T32 {
   static constexpr int kVItems = 4 * (D / 2);                 // (key quad, dim pair) items per block
   static constexpr int kVQuad = 8 * D;                        // bytes of one key quad in LDS
   // LDS slot of dim entry e inside a quad. An operand read takes entry
-  // kOc * dslot + c in lane dslot (0..31): unswizzled, lanes 8 (D = 128) or 16
-  // (D = 64) apart would hit the same banks, so the entry index within each
-  // run of kOc is XORed with dslot / (32 / kOc), and 32 lanes' 8-byte reads
-  // cover all 64 banks.
-  __device__ static int vpos(int e) { return e ^ ((e >> 5) & (kOc - 1)); }
+  // kOc * dslot + c (8 bytes) in lane dslot = 0..31; unswizzled, lanes 4 or 8
+  // (D = 128, 64) apart hit the same banks. The entry index within each run
+  // of kOc is XORed with bits of dslot chosen so that any 16 lanes cover 32
+  // four-byte banks, and any 32 lanes 64 banks, once each.
+  __device__ static int vpos(int e) {
+    return D == 128 ? e ^ (((e >> 4) ^ (e >> 6)) & 3) : e ^ (((e >> 4) ^ (e >> 5)) & 1);
+  }
 };
 static_assert(kPrefillWaves * kWave >= T32<128>::kKPieces && kPrefillWaves * kWave >= T32<128>::kVItems,
               "one staging item per thread and block");
