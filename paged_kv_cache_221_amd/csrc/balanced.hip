@@ -360,20 +360,27 @@ __device__ inline void store8(typename Ops<E, D>::storage* dst, const float* v) 
   }
 }
 
-// One wave per (request, KV head): renormalises the pieces of a segment that
-// was cut between workgroups [P1 §07: out = sum_j w_j o_j / sum_j w_j,
-// w_j = exp(lse_j - max lse), here in log2 units]. The record gives the first
-// piece slot and the piece count; each slot holds slot_rows x D floats, of
-// which the request's n * group rows are valid. Lanes take 8 consecutive
-// values of the flattened valid rows and fold kMergeBatch pieces per memory
+// Renormalises the pieces of a segment that was cut between workgroups
+// [P1 §07: out = sum_j w_j o_j / sum_j w_j, w_j = exp(lse_j - max lse), here
+// in log2 units]: merge_waves(slot_rows, D) waves per (request, KV head),
+// each taking every such wave's share of 512 values of the flattened rows.
+// The record gives the first piece slot and the piece count; each slot holds
+// slot_rows x D values, of which the request's n * group rows are valid.
+// Lanes take 8 consecutive values and fold kMergeBatch pieces per memory
 // round trip with a running maximum, so a segment of up to kMergeBatch
 // pieces costs two dependent round trips (record, then pieces).
 constexpr int kMergeBatch = 16;
+__host__ __device__ inline int merge_waves(int slot_rows, int head_dim) {
+  return (slot_rows * head_dim + kWave * 8 - 1) / (kWave * 8);
+}
 template <class E, int D>
 __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const BalancedArgs a) {
   using S = typename Ops<E, D>::storage;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int mw = merge_waves(a.slot_rows, D);
+  const int64_t wid = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int64_t unit = wid / mw;
+  const int part = (int)(wid - unit * mw);
   if (unit >= (int64_t)a.num_seqs * a.num_kv_heads) return;
   const int r = (int)(unit / a.num_kv_heads);
   const int kvh = (int)(unit - (int64_t)r * a.num_kv_heads);
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(4 * kWave) void balanced_merge_kernel(const Balance
   const int64_t sr = a.slot_rows;
   const S* po = static_cast<const S*>(a.part_o) + (int64_t)rec.x * sr * D;
   const float* pl = a.part_lse + (int64_t)rec.x * sr;
-  for (int f = lane * 8; f < n_r * g * D; f += kWave * 8) {
+  for (int f = (part * kWave + lane) * 8; f < n_r * g * D; f += mw * kWave * 8) {
     const int row = f / D, dim = f - row * D;
     float m = neg_inf(), wsum = 0.f, acc[8];
 #pragma unroll
@@ -435,8 +442,8 @@ hipError_t launch_bal(const BalancedArgs& a, hipStream_t stream) {
       <<<dim3((unsigned)(a.total_waves / NW)), dim3(NW * kWave), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
-  balanced_merge_kernel<E, D><<<dim3((unsigned)((units + 3) / 4)), dim3(4 * kWave), 0, stream>>>(a);
+  const int64_t waves = (int64_t)a.num_seqs * a.num_kv_heads * merge_waves(a.slot_rows, D);
+  balanced_merge_kernel<E, D><<<dim3((unsigned)((waves + 3) / 4)), dim3(4 * kWave), 0, stream>>>(a);
   return hipGetLastError();
 }
 
