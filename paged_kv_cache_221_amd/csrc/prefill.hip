@@ -4,7 +4,7 @@
 // prefill chunk: query row i of it sees keys 0 .. c + i (its cached context c
 // plus itself and earlier new tokens [P1 §04 causal mask]). Prefill is a dense
 // contraction [P1 §04 table: GEMM, compute-bound], so the work is arranged for
-// operand reuse: a workgroup of 4 waves owns a tile of query tokens of one
+// operand reuse: a workgroup of 8 waves owns a tile of query tokens of one
 // (request, KV head); every KV block is fetched once per workgroup into
 // double-buffered LDS through a register prefetch ring of PA_PREFILL_RING
 // blocks, and each wave reads the block's MFMA operands from LDS once for all
@@ -36,8 +36,10 @@
 #ifndef PA_PREFILL_RING
 #define PA_PREFILL_RING 4
 #endif
+// Workgroups per CU the prefill kernels are compiled for (with 8 waves: two
+// waves per SIMD)
 #ifndef PA_PREFILL_OCC
-#define PA_PREFILL_OCC 2
+#define PA_PREFILL_OCC 1
 #endif
 // Fixed cost of a tile in the equal-share prefill, in KV blocks: a piece
 // pays its query loads, pipeline fill and stores (a cut tile's fp32 partial
@@ -51,9 +53,11 @@
 namespace pa {
 namespace {
 
-// Waves per workgroup; each stages KV blocks for all of them.
+// Waves per workgroup; each stages KV blocks for all of them. Eight waves
+// (256 query rows of the 32-row tile) use each staged block twice as often
+// as four: mixed-step chunks 122 -> 120 us, the mixed step 451 -> 444 us.
 #ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 4
+#define PA_PREFILL_WAVES 8
 #endif
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;
 // Cache policy of the prefill's KV block loads (0: default; 2: nt). Several
