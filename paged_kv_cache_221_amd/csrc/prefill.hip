@@ -366,10 +366,19 @@ struct T32 {
 };
 static_assert(kPrefillWaves * kWave >= T32<128>::kKPieces && kPrefillWaves * kWave >= T32<128>::kVItems,
               "one staging item per thread and block");
+// Block pairs consumed per barrier by the 32-row tile (1 or 2). Two pairs
+// share one row maximum, reference update and rescale test, their score
+// products are independent chains, and barriers and block addressing are
+// halved: mixed-step chunks 119 -> 113 us (min), at 249 VGPRs and 100 KB of
+// LDS per workgroup.
+#ifndef PA_PF32_PAIRS
+#define PA_PF32_PAIRS 2
+#endif
+constexpr int kPf32Pairs = PA_PF32_PAIRS;
 template <int D>
 struct PfLds32 {
-  char k[2][2][kBlockTokens * T32<D>::kKRow];  // [pair buffer][block][key row]
-  char v[2][2][4 * T32<D>::kVQuad];            // [pair buffer][block][quad][dim][4 keys]
+  char k[2][2 * kPf32Pairs][kBlockTokens * T32<D>::kKRow];  // [buffer][block][key row]
+  char v[2][2 * kPf32Pairs][4 * T32<D>::kVQuad];            // [buffer][block][quad][dim][4 keys]
 };
 // One block's staging registers of a thread: a 16-byte K piece, and one dword
 // (two dims) of each of the four keys of a V quad.
@@ -481,9 +490,9 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
     }
   };
 
-  // S^T of the pair in LDS pair buffer s (keys x rows, 32 x 32)
-  auto qk = [&](int s) {
-    const char* kb = &lds.k[s][j >> 4][(j & 15) * T::kKRow + 16 * h];
+  // S^T of pair pp in LDS buffer s (keys x rows, 32 x 32)
+  auto qk = [&](int s, int pp) {
+    const char* kb = &lds.k[s][2 * pp + (j >> 4)][(j & 15) * T::kKRow + 16 * h];
     u32x4 kk[T::kQc];
 #pragma unroll
     for (int c = 0; c < T::kQc; ++c) kk[c] = *reinterpret_cast<const u32x4*>(kb + 32 * c);
@@ -492,56 +501,68 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
     for (int c = 0; c < T::kQc; ++c) acc = mma32<E>(kk[c], q[c], acc);
     return acc;
   };
-  // online softmax of one pair's scores (keys key0 .. key0 + 31): the
-  // probabilities relative to the row's reference m, and the factor for o
-  // and l when m moves
-  auto softmax = [&](const f32x16& acc, int key0, float (&p)[16], auto masked) {
+  // online softmax of NP pairs' scores (pair pp: keys key0 + 32 pp ..
+  // + 31): the probabilities relative to the row's reference m, and the
+  // factor for o and l when m moves (one maximum and one reference update
+  // for all NP pairs)
+  auto softmax = [&](const f32x16 (&acc)[kPf32Pairs], int key0, float (&p)[kPf32Pairs][16],
+                     auto masked) {
     float alpha;
     if constexpr (decltype(masked)::value) {
-      float sv[16];
+      float sv[kPf32Pairs][16];
+      float mx = neg_inf();
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int key = key0 + 8 * (t >> 2) + 4 * h + (t & 3);
-        sv[t] = key < kend ? acc[t] * scale_log2 : neg_inf();
-      }
-      float mx = sv[0];
+      for (int pp = 0; pp < kPf32Pairs; ++pp)
 #pragma unroll
-      for (int t = 1; t < 16; ++t) mx = fmax2(mx, sv[t]);
+        for (int t = 0; t < 16; ++t) {
+          const int key = key0 + 32 * pp + 8 * (t >> 2) + 4 * h + (t & 3);
+          sv[pp][t] = key < kend ? acc[pp][t] * scale_log2 : neg_inf();
+          mx = fmax2(mx, sv[pp][t]);
+        }
       mx = max_xor32(mx);
       alpha = advance_max(m, mx);
       const float m_use = m == neg_inf() ? 0.f : m;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) p[t] = fast_exp2(sv[t] - m_use);
+      for (int pp = 0; pp < kPf32Pairs; ++pp)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) p[pp][t] = fast_exp2(sv[pp][t] - m_use);
     } else {
       // every key visible and scale_log2 >= 0: the scaled maximum of the raw
       // scores is the maximum of the scaled ones, and each exponent is one
       // fused multiply-add
-      float mx = acc[0];
+      float mx = acc[0][0];
 #pragma unroll
-      for (int t = 1; t < 16; ++t) mx = fmax2(mx, acc[t]);
+      for (int pp = 0; pp < kPf32Pairs; ++pp)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) mx = fmax2(mx, acc[pp][t]);
       mx = max_xor32(mx) * scale_log2;
       alpha = advance_max(m, mx);
       const float neg_m = -m;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(acc[t], scale_log2, neg_m));
+      for (int pp = 0; pp < kPf32Pairs; ++pp)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) p[pp][t] = fast_exp2(__builtin_fmaf(acc[pp][t], scale_log2, neg_m));
     }
     return alpha;
   };
-  // l and o take the pair: rescale when the reference moved, then P.V with
-  // the values from pair buffer s
-  auto accumulate = [&](const float (&p)[16], float alpha, int s) {
+  // l and o take the pairs: rescale when the reference moved, then P.V with
+  // the values from LDS buffer s
+  auto accumulate = [&](const float (&p)[kPf32Pairs][16], float alpha, int s) {
     float ps = 0.f;
 #pragma unroll
-    for (int t = 0; t < 16; t += 4) ps += (p[t] + p[t + 1]) + (p[t + 2] + p[t + 3]);
+    for (int pp = 0; pp < kPf32Pairs; ++pp)
+#pragma unroll
+      for (int t = 0; t < 16; t += 4) ps += (p[pp][t] + p[pp][t + 1]) + (p[pp][t + 2] + p[pp][t + 3]);
     l = l * alpha + ps;
     if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int c = 0; c < T::kOc; ++c) o[c] *= alpha;
     }
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const u32x4 pk = {E::pack2(p[8 * b], p[8 * b + 1]), E::pack2(p[8 * b + 2], p[8 * b + 3]),
-                        E::pack2(p[8 * b + 4], p[8 * b + 5]), E::pack2(p[8 * b + 6], p[8 * b + 7])};
+    for (int b = 0; b < 2 * kPf32Pairs; ++b) {
+      const float* pb = &p[b >> 1][8 * (b & 1)];
+      const u32x4 pk = {E::pack2(pb[0], pb[1]), E::pack2(pb[2], pb[3]), E::pack2(pb[4], pb[5]),
+                        E::pack2(pb[6], pb[7])};
       const char* vb = &lds.v[s][b][0];
 #pragma unroll
       for (int c = 0; c < T::kOc; ++c) {
@@ -565,21 +586,29 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   // (i - b0) % RING. Blocks are consumed unconditionally, like the loads: a
   // padding block at or past b1 was read as zeros and its keys are past
   // every row's limit (kend), so it adds nothing.
+  // With kPf32Pairs == 2 a group is one step of 4 blocks and the LDS buffer
+  // alternates between groups.
+  constexpr int kStep = 2 * kPf32Pairs;  // blocks per barrier
+  static_assert(RING % kStep == 0, "whole steps per group");
   auto group = [&](int i0, auto masked) {
     const int nxt = load_ids(i0 + 2 * RING);
 #pragma unroll
-    for (int jj = 0; jj < RING; jj += 2) {
+    for (int jj = 0; jj < RING; jj += kStep) {
       const int i = i0 + jj;
-      const int s = (jj >> 1) & 1;
-      stage(ring[jj], s, 0);
-      stage(ring[jj + 1], s, 1);
+      const int s = RING / kStep >= 2 ? (jj / kStep) & 1 : ((i - b0) / kStep) & 1;
+#pragma unroll
+      for (int bb = 0; bb < kStep; ++bb) stage(ring[jj + bb], s, bb);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      issue(ring[jj], i + RING, __builtin_amdgcn_readlane(nid, jj));
-      issue(ring[jj + 1], i + 1 + RING, __builtin_amdgcn_readlane(nid, jj + 1));
+#pragma unroll
+      for (int bb = 0; bb < kStep; ++bb)
+        issue(ring[jj + bb], i + bb + RING, __builtin_amdgcn_readlane(nid, jj + bb));
       __builtin_amdgcn_sched_barrier(0);
-      float pr[16];
-      const float alpha = softmax(qk(s), i * kBlockTokens, pr, masked);
+      f32x16 acc[kPf32Pairs];
+#pragma unroll
+      for (int pp = 0; pp < kPf32Pairs; ++pp) acc[pp] = qk(s, pp);
+      float pr[kPf32Pairs][16];
+      const float alpha = softmax(acc, i * kBlockTokens, pr, masked);
       accumulate(pr, alpha, s);
     }
     nid = nxt;
