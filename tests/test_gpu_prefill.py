@@ -2,8 +2,8 @@
 workspace) and per tile (without), against the oracle.
 
 The shares cut tiles at arbitrary KV blocks, so these cases aim at the
-merge: GQA groups whose heads do not fill a power of two (3) or fill a whole
-tile row (16), a tile cut into ~190 one-block pieces (one KV head, few items:
+merge: GQA groups whose heads do not fill a power of two (3, 5, 7) or fill a
+whole tile row (16), groups of 1, 2 and 8, a tile cut into ~190 one-block pieces (one KV head, few items:
 one item per share), and a workspace reused across batches in which the same
 token positions change from prefill to decode rows, whose stale merge
 records must not touch the new batch.
@@ -29,7 +29,13 @@ def _run(st, lay, workspace, causal=True):
 
 @pytest.mark.parametrize("path", ["shares", "per-tile"])
 @pytest.mark.parametrize("case", [("bf16", 128, 6, 2, True), ("bf16", 64, 16, 1, True),
-                                  ("f16", 128, 12, 4, False), ("f32", 64, 16, 1, True)],
+                                  ("f16", 128, 12, 4, False), ("f32", 64, 16, 1, True),
+                                  # the 16-bit tile takes 32 // g tokens per wave:
+                                  # groups that leave rows of a wave unused (5, 7)
+                                  # and that fill it (1, 2, 8)
+                                  ("bf16", 128, 5, 1, True), ("f16", 64, 7, 1, True),
+                                  ("bf16", 128, 8, 8, True), ("bf16", 64, 4, 2, False),
+                                  ("f16", 128, 16, 2, True)],
                          ids=lambda c: "-".join(map(str, c)))
 def test_prefill_group_sizes(gpu_lib, case, path):
     dtype, d, hq, hkv, causal = case
