@@ -693,12 +693,42 @@ def bench_rope_write(k: int):
     print(f"[bench] rope + write: {s['median']:.4f} ms", file=sys.stderr, flush=True)
     del st, calls
     torch.cuda.empty_cache()
+    cp = _device_copy_ms(nbytes)
     return {"tokens": t, "kernel_ms": round(s["mean"], 4),
+            "device_copy_ms": round(cp, 4),
+            "frac_of_device_copy": round(cp / s["median"], 4),
             "kernel_ms_median": round(s["median"], 4), "kernel_ms_min": round(s["min"], 4),
             "GBps": round(nbytes / (s["median"] * 1e-3) / 1e9, 1),
             "frac_of_8TBps": round(nbytes / (s["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": nbytes,
             "timing": "5 runs of 48 back-to-back calls, one pair of events per run"}
+
+
+def _device_copy_ms(nbytes: int) -> float:
+    """Median time (ms) of torch's device-to-device copy of ``nbytes / 2``
+    bytes (so ``nbytes`` of read plus write traffic, like the legs it sits
+    beside), rotating over copies that together exceed the 256 MB last-level
+    cache: the rate a plain copy of the same traffic reaches on this GPU."""
+    import torch
+    half = max(16, (nbytes // 2) // 16 * 16)
+    n = max(2, (1200 << 20) // (2 * half))
+    srcs = [torch.empty(half, dtype=torch.uint8, device="cuda").random_() for _ in range(n)]
+    dsts = [torch.empty_like(x) for x in srcs]
+    for i in range(n):
+        dsts[i].copy_(srcs[i])
+    torch.cuda.synchronize()
+    runs, calls = [], 4 * n
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(calls):
+            dsts[i % n].copy_(srcs[i % n])
+        e1.record()
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1) / calls)
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return statistics.median(runs)
 
 
 def bench_copy_blocks(k: int, pairs: int = 4096):
@@ -730,7 +760,10 @@ def bench_copy_blocks(k: int, pairs: int = 4096):
           flush=True)
     del kc, vc, copy
     torch.cuda.empty_cache()
+    cp = _device_copy_ms(nbytes)
     return {"pairs": pairs, "kernel_ms": round(s["mean"], 4),
+            "device_copy_ms": round(cp, 4),
+            "frac_of_device_copy": round(cp / s["median"], 4),
             "kernel_ms_median": round(s["median"], 4), "kernel_ms_min": round(s["min"], 4),
             "GBps": round(nbytes / (s["median"] * 1e-3) / 1e9, 1),
             "frac_of_8TBps": round(nbytes / (s["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

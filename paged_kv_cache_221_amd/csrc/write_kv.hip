@@ -76,24 +76,27 @@ __global__ __launch_bounds__(kWriteThreads) void copy_blocks_kernel(
   const u32x4* vs = v_cache + src * vecs_per_block;
   u32x4* kd = k_cache + dst * vecs_per_block;
   u32x4* vd = v_cache + dst * vecs_per_block;
-  // four vectors of K and four of V in flight per thread before the stores
-  constexpr int kBatch = 4;
+  // kBatch vectors of K and as many of V in flight per thread before the
+  // stores (a whole 16-token block pair of 8 heads x 128 bf16 at 8); the
+  // copied bytes are not read again by this kernel, so they stream past the
+  // caches
+  constexpr int kBatch = 8;
   for (int64_t i0 = threadIdx.x; i0 < vecs_per_block; i0 += kBatch * kWriteThreads) {
     u32x4 a[kBatch], b[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int64_t i = i0 + j * kWriteThreads;
       if (i < vecs_per_block) {
-        a[j] = ks[i];
-        b[j] = vs[i];
+        a[j] = __builtin_nontemporal_load(ks + i);
+        b[j] = __builtin_nontemporal_load(vs + i);
       }
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int64_t i = i0 + j * kWriteThreads;
       if (i < vecs_per_block) {
-        kd[i] = a[j];
-        vd[i] = b[j];
+        __builtin_nontemporal_store(a[j], kd + i);
+        __builtin_nontemporal_store(b[j], vd + i);
       }
     }
   }
