@@ -496,6 +496,9 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
     u32x4 kk[T::kQc];
 #pragma unroll
     for (int c = 0; c < T::kQc; ++c) kk[c] = *reinterpret_cast<const u32x4*>(kb + 32 * c);
+    // all of the pair's K reads go out before its first product (left to
+    // itself the compiler waits for each read just before its product)
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 acc = {};
 #pragma unroll
     for (int c = 0; c < T::kQc; ++c) acc = mma32<E>(kk[c], q[c], acc);
