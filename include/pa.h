@@ -176,7 +176,10 @@ pa_status pa_lse_merge(void *out, float *lse_out, const float *o_part,
  *                     pa_decode_balanced_workspace_bytes(...) bytes; its
  *                     contents need not be initialised; two calls in flight
  *                     at once must not share it
- *   num_seqs        : at most 4096 (else PA_ERR_UNSUPPORTED)
+ *   num_seqs        : any; more than 4096 requests run as consecutive
+ *                     batches of at most 4096 (one launch pair each, each
+ *                     balanced over the whole GPU), and the workspace size
+ *                     is that of one such batch
  * Other arguments as for pa_decode. Too small a workspace returns
  * PA_ERR_WORKSPACE. */
 size_t pa_decode_balanced_workspace_bytes(const pa_kv_cache *cache, int num_seqs,

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -243,34 +244,32 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, const void* q, co
   if (s != PA_OK) return s;
   s = check_attention_shape(cache, num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale);
   if (s != PA_OK) return s;
-  if (num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
-  if (out == nullptr || q == nullptr || block_table == nullptr || seq_lens == nullptr)
+  if (out == nullptr || q == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      workspace == nullptr)
     return PA_ERR_NULL;
   const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
   if (tw <= 0) return PA_ERR_LAUNCH;
   const int group = num_heads / cache->num_kv_heads;
+  // Requests go in chunks of at most kMaxBalancedSeqs (the kernel's prefix
+  // sums live in LDS), one launch pair per chunk on the stream, each chunk
+  // balanced over the whole GPU; the workspace holds one chunk's partials and
+  // is reused in stream order.
+  const int chunk = std::min(num_seqs, pa::kMaxBalancedSeqs);
   const BalancedLayout lay =
-      balanced_layout(tw, group, cache->head_dim, num_seqs, cache->num_kv_heads);
-  if (workspace == nullptr) return PA_ERR_NULL;
+      balanced_layout(tw, group, cache->head_dim, chunk, cache->num_kv_heads);
   if (group > pa::kTileRows) return PA_ERR_UNSUPPORTED;
   if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   pa::BalancedArgs a{};
   a.k_cache = cache->k_cache;
   a.v_cache = cache->v_cache;
-  a.q = q;
-  a.out = out;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
   a.part_o = static_cast<void*>(ws + lay.part_o);
   a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
   a.records = reinterpret_cast<int2*>(ws + lay.records);
   a.cu_seqlens = nullptr;
-  a.num_tokens = num_seqs;
   a.causal = 0;
   a.slot_rows = group;
-  a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = cache->num_kv_heads;
   a.group = group;
@@ -280,13 +279,27 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, const void* q, co
   a.total_waves = tw;
   a.scale_log2 = scale_log2_of(cache, scale);
   a.out_scale = out_scale_of(cache);
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.slot_mapping = slot_mapping;
   a.num_slots = (int64_t)cache->num_blocks * cache->block_size;
   a.k_scale = cache->dtype == PA_FP8_E4M3 ? cache->k_scale : 1.f;
   a.v_scale = cache->dtype == PA_FP8_E4M3 ? cache->v_scale : 1.f;
-  return launched(pa::launch_balanced(a, cache->dtype, static_cast<hipStream_t>(stream)));
+  const int64_t row_bytes = (int64_t)num_heads * cache->head_dim * act_bytes(cache->dtype);
+  const int64_t new_bytes = (int64_t)cache->num_kv_heads * cache->head_dim * act_bytes(cache->dtype);
+  for (int r0 = 0; r0 < num_seqs; r0 += chunk) {
+    const int n = std::min(chunk, num_seqs - r0);
+    a.q = static_cast<const char*>(q) + r0 * row_bytes;
+    a.out = static_cast<char*>(out) + r0 * row_bytes;
+    a.block_table = block_table + (int64_t)r0 * max_blocks_per_seq;
+    a.seq_lens = seq_lens + r0;
+    a.k_new = k_new == nullptr ? nullptr : static_cast<const char*>(k_new) + r0 * new_bytes;
+    a.v_new = v_new == nullptr ? nullptr : static_cast<const char*>(v_new) + r0 * new_bytes;
+    a.slot_mapping = slot_mapping == nullptr ? nullptr : slot_mapping + r0;
+    a.num_tokens = n;
+    a.num_seqs = n;
+    const pa_status st =
+        launched(pa::launch_balanced(a, cache->dtype, static_cast<hipStream_t>(stream)));
+    if (st != PA_OK) return st;
+  }
+  return PA_OK;
 }
 
 // Scratch of pa_write_decode_balanced_noalloc: the balanced kernels'
@@ -606,8 +619,8 @@ size_t pa_decode_balanced_workspace_bytes(const pa_kv_cache* cache, int num_seqs
   if (cache->head_dim != 64 && cache->head_dim != 128) return 0;
   const int tw = total_waves(cache->dtype, cache->head_dim, cache->num_kv_heads);
   if (tw <= 0) return 0;
-  return balanced_layout(tw, num_heads / cache->num_kv_heads, cache->head_dim, num_seqs,
-                         cache->num_kv_heads)
+  return balanced_layout(tw, num_heads / cache->num_kv_heads, cache->head_dim,
+                         std::min(num_seqs, pa::kMaxBalancedSeqs), cache->num_kv_heads)
       .total;
 }
 
@@ -632,7 +645,6 @@ pa_status pa_write_decode_balanced_noalloc(const pa_kv_cache* cache, void* out, 
   if (s != PA_OK) return s;
   s = check_attention_shape(cache, num_seqs, num_heads, max_blocks_per_seq, max_seq_len, scale);
   if (s != PA_OK) return s;
-  if (num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
   if (pa_decode_balanced_workspace_bytes(cache, num_seqs, num_heads) > kScratchBytes)

@@ -183,6 +183,40 @@ def test_balanced_decode_many_short_requests(gpu_lib, dtype, hq, hkv, d):
     assert same_bits(k0, st.k_cache) and same_bits(v0, st.v_cache), "fused write differs"
 
 
+def test_balanced_decode_more_requests_than_one_batch(gpu_lib):
+    """4,300 short requests: past 4,096 the balanced decode runs consecutive
+    batches of at most 4,096 requests (q, out, tables, lengths and the fused
+    write's rows offset per batch) in one workspace sized for one batch.
+    Requests on both sides of the boundary, and at both ends, are checked
+    against the oracle on both paths; the fused write matches pa_write_kv."""
+    rng = np.random.Generator(np.random.PCG64(4300))
+    lens = rng.integers(1, 81, size=4300).tolist()
+    lay = build_layout("over-4096-requests-bf16", "bf16", lens, [1] * len(lens), num_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16, seed=43, pool_factor=1.1)
+    req = sorted(set(list(range(24)) + list(range(4080, 4112)) + list(range(4276, 4300)) +
+                     rng.choice(4300, size=24, replace=False).tolist()))
+    st, snap, _ = prepare(lay, requests=req)
+    k0, v0 = st.k_cache.clone(), st.v_cache.clone()
+    gpu_write(st)
+    snap.apply_oracle_write(lay)
+    want, _ = decode_oracle(st, snap, req)
+    ws_bytes = pa.pa_decode_balanced_workspace_bytes(st.k_cache, st.v_cache, 4300, 8)
+    assert ws_bytes == pa.pa_decode_balanced_workspace_bytes(st.k_cache, st.v_cache, 4096, 8)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    for path in ("balanced", "fused"):
+        if path == "balanced":
+            out = pa.pa_decode_balanced(st.k_cache, st.v_cache, st.q, st.block_table,
+                                        st.seq_lens, lay.max_seq_len, lay.scale, workspace=ws)
+        else:
+            out = pa.pa_write_decode_balanced(k0, v0, st.q, st.k_new, st.v_new,
+                                              st.slot_mapping, st.block_table, st.seq_lens,
+                                              lay.max_seq_len, lay.scale, workspace=ws)
+        torch.cuda.synchronize()
+        check_close(gpu_rows(out, "bf16")[req], want[req], "bf16",
+                    label=f"{lay.name} {path}: {len(req)} of 4300 requests")
+    assert same_bits(k0, st.k_cache) and same_bits(v0, st.v_cache), "fused write differs"
+
+
 def test_balanced_decode_empty_requests_and_reuse(gpu_lib):
     lay = small_decode(41, dtype="bf16", batch=8, min_len=50, max_len=3000, num_heads=32,
                        num_kv_heads=8)
