@@ -40,7 +40,9 @@
  *   Results for such inputs are unspecified. The Python package's
  *   validate_metadata() checks the whole contract on the host (a debug aid:
  *   it copies the arrays from the device).
- * - Supported now: block_size 16; head_dim 64 or 128; Hq % Hkv == 0 with
+ * - Supported now: block_size 16, 32, 64, 128 or 256 (the kernels walk
+ *   16-token blocks: a cache block of 16 << s tokens is read as 2^s
+ *   consecutive ones); head_dim 64 or 128; Hq % Hkv == 0 with
  *   Hq / Hkv <= 16; fp32, fp16 and bf16 storage with fp32 accumulation, and
  *   E4M3 KV caches (bf16 arithmetic on the exactly widened codes) in every
  *   entry point.

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const At
     n = hi - lo;
   }
   int seq_len = a.seq_lens[r];
-  seq_len = min(max(seq_len, 0), a.max_blocks * kBlockTokens);
+  seq_len = min(max(seq_len, 0), (a.max_blocks * kBlockTokens) << a.block_shift);
   const int g = a.group;
   const int ctx = max(seq_len - n, 0);
   const int row = lane & 15;
@@ -60,6 +60,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void paged_attention_kernel(const At
   view.rs = (int64_t)a.num_kv_heads * D;
   view.table = a.block_table + (int64_t)r * a.max_blocks;
   view.num_blocks = a.num_blocks;
+  view.shift = a.block_shift;
 
   typename O::Q qop;
   RowState<D> st;
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(NW * kWave, PA_COAL_OCC) void coalesced_attention_k
   const int hg = u % groups;
   const int r = u / groups;
   const int kvh = hg * NW + wave;
-  const int seq_len = min(max(a.seq_lens[r], 0), a.max_blocks * kBlockTokens);
+  const int seq_len = min(max(a.seq_lens[r], 0), (a.max_blocks * kBlockTokens) << a.block_shift);
   const int g = a.group;
   const int row = lane & 15, grp = lane >> 4;
   const bool valid = row < g;
@@ -196,6 +197,7 @@ __global__ __launch_bounds__(NW * kWave, PA_COAL_OCC) void coalesced_attention_k
   view.rs = (int64_t)a.num_kv_heads * D;
   view.table = a.block_table + (int64_t)r * a.max_blocks;
   view.num_blocks = a.num_blocks;
+  view.shift = a.block_shift;
 
   typename O::Q qop;
   O::load_q(qop, static_cast<const S*>(a.q) + ((int64_t)r * a.num_heads + head) * D, valid, lane);

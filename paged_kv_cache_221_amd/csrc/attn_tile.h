@@ -840,8 +840,16 @@ struct KvView {
   const Storage* v;        // v_cache + kv_head * D
   int64_t rs;              // elements between consecutive keys: Hkv * D
   const int32_t* table;    // this request's block-table row
-  int num_blocks;          // pool size, for the out-of-pool guard
+  int num_blocks;          // pool size in cache blocks, for the out-of-pool guard
+  int shift;               // cache blocks hold 16 << shift tokens
 };
+
+// The pool's 16-token block holding 16-token block `li` of a request whose
+// table entry for it is `e` (cache blocks of 16 << shift tokens), or -1 when
+// the entry is outside the pool (checked before the shift can overflow).
+__device__ inline int block16(int e, int li, int shift, int num_blocks) {
+  return (e >= 0 && e < num_blocks) ? (e << shift) + (li & ((1 << shift) - 1)) : -1;
+}
 
 // One block: mask, online softmax update, P.V accumulation. Keys at or past
 // seq_len were read as zeros (the buffer range stops there); keys at or past
@@ -1048,11 +1056,12 @@ __device__ inline void stream_blocks(RowState<D>& st, const typename Ops<E, D>::
   const int64_t block_elems = (int64_t)kBlockTokens * kv_view.rs;
   const int row_bytes = (int)(kv_view.rs * (int64_t)sizeof(S));
   const __attribute__((address_space(4))) int32_t* tab =
-      (const __attribute__((address_space(4))) int32_t*)(kv_view.table + b_begin);
+      (const __attribute__((address_space(4))) int32_t*)kv_view.table;
 
   auto load = [&](KV& kv, int i) {
-    const int pb = tab[min(i, n - 1)];
-    const bool ok = i < n && pb >= 0 && pb < kv_view.num_blocks;
+    const int li = b_begin + min(i, n - 1);
+    const int pb = block16(tab[li >> kv_view.shift], li, kv_view.shift, kv_view.num_blocks);
+    const bool ok = i < n && pb >= 0;
     const int keys = min(seq_len - (b_begin + i) * kBlockTokens, kBlockTokens);
     const int range = ok ? keys * row_bytes : 0;
     const int64_t base = (int64_t)(ok ? pb : 0) * block_elems;

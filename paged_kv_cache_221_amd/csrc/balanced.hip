@@ -167,7 +167,7 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int B = a.num_seqs;
-  const int max_len = a.max_blocks * kBlockTokens;
+  const int max_len = (a.max_blocks * kBlockTokens) << a.block_shift;
 
   // 1. prefix sums of per-request item counts (blocks plus the fixed cost of
   //    a segment, per head group), in LDS
@@ -266,6 +266,7 @@ __global__ __launch_bounds__(NW * kWave, PA_BAL_OCC) void balanced_decode_kernel
     view.rs = (int64_t)hkv * D;
     view.table = a.block_table + (int64_t)r * a.max_blocks;
     view.num_blocks = a.num_blocks;
+    view.shift = a.block_shift;
 
     const int head = kvh * g + (row_valid ? hh : 0);
     const int64_t qrow = (int64_t)q_lo + (row_valid ? tok : 0);

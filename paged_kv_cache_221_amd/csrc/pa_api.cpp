@@ -49,6 +49,14 @@ float scale_log2_of(const pa_kv_cache* c, float scale) {
 }
 float out_scale_of(const pa_kv_cache* c) { return c->dtype == PA_FP8_E4M3 ? c->v_scale : 1.0f; }
 
+// log2(block_size / 16) for the supported cache block sizes 16, 32, ... 256
+// (the kernels walk 16-token blocks), else -1
+int block_shift_of(int block_size) {
+  for (int s = 0; s <= 4; ++s)
+    if (block_size == (kSupportedBlock << s)) return s;
+  return -1;
+}
+
 pa_status check_attention_shape(const pa_kv_cache* c, int num_seqs, int num_heads,
                                 int max_blocks_per_seq, int max_seq_len, float scale) {
   if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
@@ -56,7 +64,7 @@ pa_status check_attention_shape(const pa_kv_cache* c, int num_seqs, int num_head
   if (num_heads % c->num_kv_heads != 0) return PA_ERR_SHAPE;
   if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * c->block_size) return PA_ERR_SHAPE;
   if (!isfinite(scale)) return PA_ERR_SHAPE;
-  if (c->block_size != kSupportedBlock) return PA_ERR_UNSUPPORTED;
+  if (block_shift_of(c->block_size) < 0) return PA_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (num_heads / c->num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
   return PA_OK;
@@ -85,6 +93,7 @@ AttnArgs base_args(const pa_kv_cache* c, const void* q, const int32_t* block_tab
   a.out_scale = out_scale_of(c);
   a.causal = 1;
   a.pf_shares = 0;  // prefill: one workgroup per tile unless a workspace holds partials
+  a.block_shift = block_shift_of(c->block_size);
   return a;
 }
 
@@ -282,6 +291,7 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, const void* q, co
   a.num_slots = (int64_t)cache->num_blocks * cache->block_size;
   a.k_scale = cache->dtype == PA_FP8_E4M3 ? cache->k_scale : 1.f;
   a.v_scale = cache->dtype == PA_FP8_E4M3 ? cache->v_scale : 1.f;
+  a.block_shift = block_shift_of(cache->block_size);
   const int64_t row_bytes = (int64_t)num_heads * cache->head_dim * act_bytes(cache->dtype);
   const int64_t new_bytes = (int64_t)cache->num_kv_heads * cache->head_dim * act_bytes(cache->dtype);
   for (int r0 = 0; r0 < num_seqs; r0 += chunk) {
@@ -416,7 +426,7 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, const void* q,
   a.out = out;
   a.num_tokens = num_seqs;
   const int max_blocks = (max_seq_len + kSupportedBlock - 1) / kSupportedBlock;
-  a.split_blocks = max_blocks_per_seq;
+  a.split_blocks = max_blocks_per_seq << a.block_shift;
   const int64_t grid = (int64_t)num_seqs * cache->num_kv_heads;
   const int nw = coalesced_group(cache, num_seqs);
   if (nw > 0)
@@ -468,7 +478,7 @@ pa_status pa_decode_splitk(const pa_kv_cache* cache, float* o_part, float* lse_p
   a.lse_part = lse_part;
   a.num_tokens = num_seqs;
   a.num_splits = pa_splitk_num_splits(max_seq_len, split_tokens);
-  a.split_blocks = split_tokens / cache->block_size;
+  a.split_blocks = split_tokens / kSupportedBlock;  // 16-token blocks
   const int64_t grid = (int64_t)num_seqs * cache->num_kv_heads * a.num_splits;
   if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
   const int nw = coalesced_group(cache, (int64_t)num_seqs * a.num_splits);
@@ -540,7 +550,7 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
   a.cu_seqlens = cu_seqlens_q;
   a.num_tokens = num_tokens;
   a.causal = causal;
-  a.split_blocks = max_blocks_per_seq;
+  a.split_blocks = max_blocks_per_seq << a.block_shift;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool use_ws = workspace != nullptr && num_seqs <= pa::kMaxBalancedSeqs;
   VarlenLayout vl{};
@@ -601,6 +611,7 @@ pa_status pa_varlen(const pa_kv_cache* cache, void* out, const void* q,
     b.total_waves = tw;
     b.scale_log2 = a.scale_log2;
     b.out_scale = a.out_scale;
+    b.block_shift = a.block_shift;
     return launched(pa::launch_balanced(b, cache->dtype, st));
   }
   a.num_tiles = 1;

@@ -40,6 +40,10 @@ struct AttnArgs {
   float* pf_lse;             // [2 * pf_shares, prefill_rows] partial LSEs (log2 domain)
   int4* pf_rec;              // [T, Hkv] per token: (first slot, pieces, row in slot, 0)
   int pf_shares;
+  // Cache blocks hold 16 << block_shift tokens; the kernels walk 16-token
+  // blocks: block i of a request is rows 16 (i mod 2^s) .. + 15 of table
+  // entry i >> s, i.e. 16-token block (entry << s) + (i mod 2^s) of the pool.
+  int block_shift;
 };
 
 struct MergeArgs {
@@ -109,6 +113,7 @@ struct BalancedArgs {
   int64_t num_slots;
   float k_scale;             // E4M3 quantisation scales of the write
   float v_scale;
+  int block_shift;           // as in AttnArgs
 };
 
 // Waves per workgroup the attention kernel is built for.

@@ -98,7 +98,7 @@ __device__ inline PfRequest pf_request(const AttnArgs& a, int r) {
   PfRequest q;
   q.q_lo = lo;
   q.n = hi - lo;
-  q.seq_len = min(max(a.seq_lens[r], 0), a.max_blocks * kBlockTokens);
+  q.seq_len = min(max(a.seq_lens[r], 0), (a.max_blocks * kBlockTokens) << a.block_shift);
   q.ctx = max(q.seq_len - q.n, 0);
   return q;
 }
@@ -180,8 +180,9 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
   const __attribute__((address_space(4))) int32_t* tab =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)r * a.max_blocks);
   auto issue = [&](typename St::Regs& rg, int i) {
-    const int pb = tab[min(i, b1 - 1)];
-    const bool ok = i < b1 && pb >= 0 && pb < a.num_blocks;
+    const int li = min(i, b1 - 1);
+    const int pb = block16(tab[li >> a.block_shift], li, a.block_shift, a.num_blocks);
+    const bool ok = i < b1 && pb >= 0;
     const int keys = min(seq_len - i * kBlockTokens, kBlockTokens);
     const int range = ok ? keys * row_bytes_g : 0;
     const int64_t base = (int64_t)(ok ? pb : 0) * block_elems;
@@ -464,9 +465,13 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   // result would then wait for them too.
   const __attribute__((address_space(1))) int32_t* tabv =
       (const __attribute__((address_space(1))) int32_t*)(a.block_table + (int64_t)r * a.max_blocks);
-  auto load_ids = [&](int first) { return tabv[min(first + (lane & (RING - 1)), b1 - 1)]; };
+  auto load_ids = [&](int first) {
+    const int li = min(first + (lane & (RING - 1)), b1 - 1);
+    return block16(tabv[li >> a.block_shift], li, a.block_shift, a.num_blocks);
+  };
+  // pb: the pool's 16-token block, or -1 (outside the pool)
   auto issue = [&](Regs32& rg, int i, int pb) {
-    const bool ok = i < b1 && pb >= 0 && pb < a.num_blocks;
+    const bool ok = i < b1 && pb >= 0;
     const int keys = min(seq_len - i * kBlockTokens, kBlockTokens);
     const int range = ok ? keys * row_bytes_g : 0;
     const int64_t base = (int64_t)(ok ? pb : 0) * block_elems;
@@ -580,7 +585,10 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   int nid = load_ids(b0 + RING);  // lane k: the id of the block the group's load k reads
   Regs32 ring[RING];
 #pragma unroll
-  for (int jj = 0; jj < RING; ++jj) issue(ring[jj], b0 + jj, tab[min(b0 + jj, b1 - 1)]);
+  for (int jj = 0; jj < RING; ++jj) {
+    const int li = min(b0 + jj, b1 - 1);
+    issue(ring[jj], b0 + jj, block16(tab[li >> a.block_shift], li, a.block_shift, a.num_blocks));
+  }
   // take the ids in here (a wait for the one load issued before the ring's):
   // entering the loop with the load still pending makes the compiler wait
   // for nearly every load at the top of each group

@@ -74,7 +74,10 @@ def test_validation_codes(lib):
                          None) == -3
     # unsupported head_dim / block size / group
     assert lib.pa_decode(byref(_cache(d=96)), one, one, one, one, 1, 8, 4, 64, 0.1, None) == -4
-    assert lib.pa_decode(byref(_cache(bs=32)), one, one, one, one, 1, 8, 4, 64, 0.1, None) == -4
+    # cache blocks of 16 << s tokens (s = 0 .. 4) are supported, others are not
+    for bs in (8, 24, 48, 512):
+        assert lib.pa_decode(byref(_cache(bs=bs)), one, one, one, one, 1, 8, 8, 64, 0.1,
+                             None) == -4
     assert lib.pa_decode(byref(_cache(hkv=1)), one, one, one, one, 1, 32, 4, 64, 0.1,
                          None) == -4
     # zero requests: nothing to do

@@ -112,14 +112,14 @@ def small_decode(seed: int, dtype: str = "bf16", batch: int = 6, min_len: int = 
                  max_len: int = 300, num_heads: int = 8, num_kv_heads: int = 2,
                  head_dim: int = 128, pool_factor: float = 1.5,
                  split_tokens: int | None = None, value_std: float = 1.0,
-                 key_outlier_frac: float = 0.0) -> StepLayout:
+                 key_outlier_frac: float = 0.0, block_size: int = 16) -> StepLayout:
     """A decode step small enough for the oracle in well under a second, with
     lengths that span several blocks and end in ragged tails."""
     rng = np.random.Generator(np.random.PCG64(seed + 1000))
     lens = rng.integers(min_len, max_len, size=batch, endpoint=True)
     return build_layout(f"small-decode-{dtype}-s{seed}", dtype, lens, [1] * batch,
                         num_heads=num_heads, num_kv_heads=num_kv_heads,
-                        head_dim=head_dim, block_size=16, seed=seed,
+                        head_dim=head_dim, block_size=block_size, seed=seed,
                         pool_factor=pool_factor, value_std=value_std,
                         key_outlier_frac=key_outlier_frac, key_outlier_scale=8.0,
                         split_tokens=split_tokens)
@@ -129,13 +129,13 @@ def small_varlen(seed: int, dtype: str = "bf16", prefill=((40, 0), (70, 33), (17
                  decode_lens=(1, 15, 16, 17, 200), num_heads: int = 8,
                  num_kv_heads: int = 2, head_dim: int = 128, pool_factor: float = 1.3,
                  value_std: float = 1.0, shared_prefix_blocks: int = 0,
-                 sharers=()) -> StepLayout:
+                 sharers=(), block_size: int = 16) -> StepLayout:
     """A mixed step: ``prefill`` lists (query_len, context) pairs, then decode
     requests with the given KV lengths."""
     lens = [n + c for n, c in prefill] + list(decode_lens)
     qlens = [n for n, _ in prefill] + [1] * len(decode_lens)
     return build_layout(f"small-varlen-{dtype}-s{seed}", dtype, lens, qlens,
                         num_heads=num_heads, num_kv_heads=num_kv_heads,
-                        head_dim=head_dim, block_size=16, seed=seed,
+                        head_dim=head_dim, block_size=block_size, seed=seed,
                         pool_factor=pool_factor, value_std=value_std,
                         shared_prefix_blocks=shared_prefix_blocks, sharers=sharers)
