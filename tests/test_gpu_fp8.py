@@ -173,6 +173,41 @@ def test_fp8_prefill_chunks(gpu_lib, case, path):
                 label=f"{lay.name} e4m3 prefill {path}")
 
 
+@pytest.mark.parametrize("bs", [32, 256])
+def test_fp8_cache_blocks_larger_than_16(gpu_lib, bs):
+    """An E4M3 cache with 32- or 256-token blocks: the balanced decode, the
+    per-request decode and a varlen step with prefill chunks (both prefill
+    kernels) read each cache block as consecutive 16-token blocks."""
+    lay = small_varlen(990 + bs, dtype="bf16", num_heads=16, num_kv_heads=4, head_dim=128,
+                       prefill=((60, bs + 3), (33, 0)), decode_lens=(1, bs, 2 * bs + 9, 17),
+                       block_size=bs)
+    s = _Fp8Step(lay, 0.0625, 0.04)
+    s.write()
+    st = s.st
+    want, _ = oracle.paged_varlen(s.q, s.k, s.v, lay.cu_seqlens_q, lay.seq_lens,
+                                  lay.block_table, lay.scale, lay.block_size, "bf16",
+                                  kv_dtype="e4m3", k_scale=s.ks, v_scale=s.vs)
+    for path in ("shares", "direct"):
+        out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                           st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale,
+                           workspace="auto" if path == "shares" else None, **s.kw())
+        torch.cuda.synchronize()
+        check_close(gpu_rows(out, "bf16"), want, "bf16",
+                    groups=request_groups(lay, range(lay.num_seqs)),
+                    label=f"{lay.name} e4m3 bs={bs} varlen {path}")
+    dec = small_decode(995 + bs, dtype="bf16", batch=5, min_len=1, max_len=3 * bs + 21,
+                       num_heads=8, num_kv_heads=2, head_dim=64, block_size=bs)
+    d = _Fp8Step(dec, 0.05, 0.03)
+    d.write()
+    want_d, _ = d.decode_oracle()
+    for fn in (pa.pa_decode, pa.pa_decode_balanced):
+        out = fn(d.st.k_cache, d.st.v_cache, d.st.q, d.st.block_table, d.st.seq_lens,
+                 dec.max_seq_len, dec.scale, **d.kw())
+        torch.cuda.synchronize()
+        check_close(gpu_rows(out, "bf16"), want_d, "bf16",
+                    label=f"{dec.name} e4m3 bs={bs} {fn.__name__}")
+
+
 def _bf16_rne(x32: np.ndarray) -> np.ndarray:
     """fp32 values -> bf16 bits, round to nearest even."""
     u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
