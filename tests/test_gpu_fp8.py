@@ -8,6 +8,8 @@ the fp64 oracle over the dequantised values the error is the bf16 path's
 (bf16 probabilities, fp32 sums), so the bf16 bound 2e-2 applies.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,7 +18,7 @@ import oracle
 import paged_kv_cache_221_amd as pa
 from oracle import fp8
 from oracle.block_manager import copy_blocks
-from workloads import small_decode, small_varlen
+from workloads import build_layout, small_decode, small_varlen
 from workloads.tensors import materialize_e4m3, raw_bits
 
 from _parity import check_close, gpu_rows, max_err, request_groups
@@ -206,6 +208,52 @@ def test_fp8_cache_blocks_larger_than_16(gpu_lib, bs):
         torch.cuda.synchronize()
         check_close(gpu_rows(out, "bf16"), want_d, "bf16",
                     label=f"{dec.name} e4m3 bs={bs} {fn.__name__}")
+
+
+_SWEEP = int(os.environ.get("PA_SWEEP_SEEDS", "0")) or 6
+
+
+@pytest.mark.parametrize("seed", range(_SWEEP))
+def test_fp8_sweep(gpu_lib, seed):
+    """Seeded random E4M3 steps: GQA shape, head dim, cache block size,
+    scales, ragged decode lengths with outliers, and one or two prefill
+    chunks; the balanced decode on the decode batch and the equal-share
+    varlen step on the mixed one, against the oracle over dequantised values.
+    PA_SWEEP_SEEDS=n runs n cases."""
+    rng = np.random.Generator(np.random.PCG64(8800 + seed))
+    hq, hkv, d = [(32, 8, 128), (16, 4, 64), (8, 8, 128), (16, 2, 128)][seed % 4]
+    bs = [16, 32, 16, 64, 256][seed % 5]
+    ks, vs = float(rng.choice([0.02, 0.0625, 0.2])), float(rng.choice([0.03, 0.05, 0.125]))
+    b = int(rng.choice([1, 3, 9, 40]))
+    lens = rng.integers(1, 500, size=b)
+    lens[rng.random(b) < 0.1] = 2500
+    dec = build_layout(f"fp8-sweep-{seed}", "bf16", lens.tolist(), [1] * b, num_heads=hq,
+                       num_kv_heads=hkv, head_dim=d, block_size=bs, seed=8800 + seed,
+                       pool_factor=1.3)
+    s = _Fp8Step(dec, ks, vs)
+    s.write()
+    out = pa.pa_decode_balanced(s.st.k_cache, s.st.v_cache, s.st.q, s.st.block_table,
+                                s.st.seq_lens, dec.max_seq_len, dec.scale, **s.kw())
+    torch.cuda.synchronize()
+    want, _ = s.decode_oracle()
+    tag = f"seed {seed}: {b} requests {hq}/{hkv}/{d} bs {bs} scales {ks}/{vs}"
+    check_close(gpu_rows(out, "bf16"), want, "bf16", label=f"{tag} balanced")
+    pre = [(int(rng.integers(17, 200)), int(rng.integers(0, 400)))
+           for _ in range(int(rng.integers(1, 3)))]
+    mix = small_varlen(8900 + seed, dtype="bf16", num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       prefill=pre, decode_lens=tuple(int(x) for x in lens[:5]), block_size=bs)
+    m = _Fp8Step(mix, ks, vs)
+    m.write()
+    out = pa.pa_varlen(m.st.k_cache, m.st.v_cache, m.st.q, m.st.cu_seqlens_q, m.st.seq_lens,
+                       m.st.block_table, mix.max_query_len, mix.max_seq_len, mix.scale,
+                       workspace="auto", **m.kw())
+    torch.cuda.synchronize()
+    want, _ = oracle.paged_varlen(m.q, m.k, m.v, mix.cu_seqlens_q, mix.seq_lens,
+                                  mix.block_table, mix.scale, mix.block_size, "bf16",
+                                  kv_dtype="e4m3", k_scale=m.ks, v_scale=m.vs)
+    check_close(gpu_rows(out, "bf16"), want, "bf16",
+                groups=request_groups(mix, range(mix.num_seqs)),
+                label=f"{tag} varlen prefill {pre}")
 
 
 def _bf16_rne(x32: np.ndarray) -> np.ndarray:
