@@ -328,7 +328,7 @@ def oracle_sample(st, layout, requests, kind: str, split_tokens=None, kv=None):
         oracle.lse_merge(o[requests], lse[requests])
     else:
         oracle.paged_varlen(q, k, v, layout.cu_seqlens_q, layout.seq_lens, layout.block_table,
-                            layout.scale, bs, dt, requests=requests)
+                            layout.scale, bs, dt, requests=requests, **extra)
     dt_s = time.perf_counter() - t0
     kvb = 2 * layout.num_kv_heads * layout.head_dim * (1 if kv else layout.elem_bytes)
     toks = int(np.asarray(layout.seq_lens)[requests].sum())
@@ -408,6 +408,7 @@ def read_ceiling(copies, layout, k: int):
 # ---------------------------------------------------------------- secondary legs
 SECONDARY_LEGS = ("tiny-decode-fp32", "long-context-splitk-bf16", "llama2-7b-mha-decode-fp16",
                   "mixed-step-bf16", "mixed-step-prefill-chunks-bf16",
+                  "mixed-step-prefill-chunks-e4m3-cache",
                   "llama3-8b-decode-e4m3-cache", "llama3-8b-spec-verify-q4-bf16",
                   "rope-write-kv-mixed-step-bf16", "copy-on-write-blocks-bf16",
                   "block-manager-host")
@@ -501,6 +502,7 @@ def secondary(args, only=None):
         torch.cuda.empty_cache()
     for name, leg in (("tiny-decode-fp32", bench_tiny),
                       ("mixed-step-prefill-chunks-bf16", bench_prefill_only),
+                      ("mixed-step-prefill-chunks-e4m3-cache", bench_prefill_only_fp8),
                       ("llama3-8b-decode-e4m3-cache", bench_fp8_decode),
                       ("llama3-8b-spec-verify-q4-bf16", bench_spec_verify),
                       ("rope-write-kv-mixed-step-bf16", bench_rope_write),
@@ -535,15 +537,21 @@ def bench_tiny(k: int):
     return res
 
 
-def bench_prefill_only(k: int):
+def bench_prefill_only(k: int, kv=None):
     """pa_varlen on the mixed step's 4 prefill chunks alone: the compute rate
-    of the prefill rows, exact causal FLOPs against the bf16 MFMA peak."""
+    of the prefill rows, exact causal FLOPs against the bf16 MFMA peak. With
+    ``kv`` (dtype "e4m3" and the two scales) the cache holds E4M3 codes."""
     import torch
     import paged_kv_cache_221_amd as pa
     from workloads import mixed_step_prefill_only
-    from workloads.tensors import materialize
+    from workloads.tensors import materialize, materialize_e4m3
     lay = mixed_step_prefill_only()
-    st = materialize(lay, "cuda", poison=False)
+    if kv is None:
+        st = materialize(lay, "cuda", poison=False)
+        scales = {}
+    else:
+        st = materialize_e4m3(lay, "cuda", kv["k_scale"], kv["v_scale"], poison=False)
+        scales = dict(k_scale=kv["k_scale"], v_scale=kv["v_scale"])
     out = torch.empty_like(st.q)
     ws = torch.empty(pa.pa_varlen_workspace_bytes(st.k_cache, st.v_cache, lay.num_seqs,
                                                   st.q.shape[0], lay.num_heads,
@@ -551,7 +559,7 @@ def bench_prefill_only(k: int):
                      dtype=torch.uint8, device="cuda")
     attn = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
                         st.block_table, lay.max_query_len, lay.max_seq_len, lay.scale, out=out,
-                        workspace=ws, prepared=True)
+                        workspace=ws, prepared=True, **scales)
 
     def step(ev=None):
         if ev is not None:
@@ -562,8 +570,9 @@ def bench_prefill_only(k: int):
     _, _, kern = time_steps([step], max(k, 10), 3, True)
     s = _stats(kern)
     flops = causal_flops(lay)
-    print(f"[bench] prefill chunks: median {s['median']:.4f} ms", file=sys.stderr, flush=True)
-    sample = oracle_sample(st, lay, [0], "varlen")
+    print(f"[bench] prefill chunks{'' if kv is None else ' (e4m3)'}: median {s['median']:.4f} ms",
+          file=sys.stderr, flush=True)
+    sample = oracle_sample(st, lay, [0], "varlen", kv=kv)
     del st, out, ws, attn
     torch.cuda.empty_cache()
     tflops = flops / (s["median"] * 1e-3) / 1e12
@@ -571,6 +580,12 @@ def bench_prefill_only(k: int):
             "kernel_ms_min": round(s["min"], 4), "flops": flops, "TFLOPs": round(tflops, 1),
             "frac_of_bf16_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
             "cpu_oracle": sample}
+
+
+def bench_prefill_only_fp8(k: int):
+    """The mixed step's 4 prefill chunks on an E4M3 cache (bf16 q and
+    output): the same FLOPs, with the KV codes widened to bf16 operands."""
+    return bench_prefill_only(k, kv=dict(dtype="e4m3", k_scale=0.0625, v_scale=0.0625))
 
 
 def bench_fp8_decode(k: int, copies: int = 4):

@@ -269,26 +269,6 @@ struct Ops16 {
       }
     }
   }
-  // Same operand layout, read from a block staged in LDS: rows of `row_bytes`
-  // bytes, K rows then V rows in separate arrays.
-  __device__ static void load_lds(KV& kv, const char* kb, const char* vb, int row_bytes,
-                                  int lane) {
-    const int m = lane & 15, grp = lane >> 4;
-#pragma unroll
-    for (int c = 0; c < kQk; ++c)
-      kv.k[c] = *reinterpret_cast<const u32x4*>(kb + m * row_bytes + (32 * c + 8 * grp) * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const char* src = vb + (4 * grp + i) * row_bytes + kVe * m * 2;
-      if constexpr (kVe == 8) {
-        u32x4 t = *reinterpret_cast<const u32x4*>(src);
-        kv.v[i].w[0] = t.x; kv.v[i].w[1] = t.y; kv.v[i].w[2] = t.z; kv.v[i].w[3] = t.w;
-      } else {
-        u32x2 t = *reinterpret_cast<const u32x2*>(src);
-        kv.v[i].w[0] = t.x; kv.v[i].w[1] = t.y;
-      }
-    }
-  }
   __device__ static void load_q(Q& q, const storage* qrow, bool valid, int lane) {
     const int grp = lane >> 4;
 #pragma unroll
@@ -449,26 +429,6 @@ struct Ops<Fp8, D> : Ops16<Bf16, D> {
         kv.v[i][1] = t.y;
       } else {
         kv.v[i][0] = buf_load4<kKvAux>(vr, o.v[i]);
-      }
-    }
-  }
-  // Same operand layout, from a block staged in LDS as codes (rows of
-  // `row_bytes` bytes, K rows then V rows in separate arrays).
-  __device__ static void load_lds(KV& kv, const char* kb, const char* vb, int row_bytes,
-                                  int lane) {
-    const int m = lane & 15, grp = lane >> 4;
-#pragma unroll
-    for (int j = 0; j < kK16; ++j)
-      kv.k[j] = *reinterpret_cast<const u32x4*>(kb + m * row_bytes + 16 * (grp + 4 * j));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const char* src = vb + (4 * grp + i) * row_bytes + kVe * m;
-      if constexpr (kVe == 8) {
-        const u32x2 t = *reinterpret_cast<const u32x2*>(src);
-        kv.v[i][0] = t.x;
-        kv.v[i][1] = t.y;
-      } else {
-        kv.v[i][0] = *reinterpret_cast<const unsigned*>(src);
       }
     }
   }
@@ -945,83 +905,6 @@ __device__ inline void consume_block_tiles(RowState<D> (&st)[RT], const typename
   const typename O::VA va = O::build_v(kv);
 #pragma unroll
   for (int t = 0; t < RT; ++t) O::pv_with(st[t].o, va, pk[t]);
-}
-
-// Two consecutive blocks (32 keys) against RT row tiles, 16-bit operands
-// only. P.V then runs as 16x16x32 products (the full-rate form; the 16x16x16
-// one of a single block does half the work per cycle): contraction index
-// 8 * grp + j stands for key 4 * grp + (j & 3) of the first block (j < 4) or
-// of the second (j >= 4), in both the P and the V operand, so each operand is
-// the two blocks' 16x16x16 operands side by side. The row maximum, the
-// reference update and the rescale test run once per pair. MASK as in
-// consume_block_tiles, over both blocks.
-template <class E, int D, int RT, bool MASK = true>
-__device__ inline void consume_pair_tiles(RowState<D> (&st)[RT], const typename Ops<E, D>::KV& kv0,
-                                          const typename Ops<E, D>::KV& kv1,
-                                          const typename Ops<E, D>::Q (&q)[RT], int key0,
-                                          const int (&key_end)[RT], float scale_log2, int lane) {
-  using O = Ops<E, D>;
-  static_assert(sizeof(typename O::storage) == 2, "pairs are for 16-bit operands");
-  const int grp = lane >> 4;
-  f32x4 acc0[RT], acc1[RT];
-#pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    acc0[t] = O::scores(kv0, q[t]);
-    acc1[t] = O::scores(kv1, q[t]);
-  }
-  u32x4 pk[RT];
-  float alpha[RT];
-  bool moved = false;
-#pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    float p[8];
-    if constexpr (MASK) {
-      float s[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key0 + 4 * grp + i;
-        s[i] = key < key_end[t] ? acc0[t][i] * scale_log2 : neg_inf();
-        s[4 + i] = key + kBlockTokens < key_end[t] ? acc1[t][i] * scale_log2 : neg_inf();
-      }
-      float mx = fmax2(fmax2(fmax2(s[0], s[1]), fmax2(s[2], s[3])),
-                       fmax2(fmax2(s[4], s[5]), fmax2(s[6], s[7])));
-      mx = max_xor16(mx);
-      mx = max_xor32(mx);
-      alpha[t] = advance_max(st[t].m, mx);
-      const float m_use = st[t].m == neg_inf() ? 0.f : st[t].m;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s[i] - m_use);
-    } else {
-      float mx = fmax2(fmax2(fmax2(acc0[t][0], acc0[t][1]), fmax2(acc0[t][2], acc0[t][3])),
-                       fmax2(fmax2(acc1[t][0], acc1[t][1]), fmax2(acc1[t][2], acc1[t][3])));
-      mx = max_xor16(mx);
-      mx = max_xor32(mx) * scale_log2;
-      alpha[t] = advance_max(st[t].m, mx);
-      const float neg_m = -st[t].m;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(__builtin_fmaf(acc0[t][i], scale_log2, neg_m));
-        p[4 + i] = fast_exp2(__builtin_fmaf(acc1[t][i], scale_log2, neg_m));
-      }
-    }
-    moved = moved || alpha[t] != 1.0f;
-    st[t].l = st[t].l * alpha[t] + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-    pk[t] = u32x4{E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]),
-                  E::pack2(p[6], p[7])};
-  }
-  if (__any(moved)) {
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) st[t].o[c] *= alpha[t];
-  }
-  const typename O::VA va0 = O::build_v(kv0), va1 = O::build_v(kv1);
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    const u32x4 a = u32x4{va0.a[c].x, va0.a[c].y, va1.a[c].x, va1.a[c].y};
-#pragma unroll
-    for (int t = 0; t < RT; ++t) st[t].o[c] = E::mma_qk(a, pk[t], st[t].o[c]);
-  }
 }
 
 // Streams this wave's contiguous run of n blocks, starting at logical block

@@ -8,11 +8,11 @@
 // (request, KV head); every KV block is fetched once per workgroup into
 // double-buffered LDS through a register prefetch ring of PA_PREFILL_RING
 // blocks, and each wave reads the block's MFMA operands from LDS once for all
-// of its rows. bf16 and fp16 caches give each wave 32 rows and consume blocks
-// in pairs on 32x32x16 products (pf_piece32); E4M3 caches give it RT row
-// tiles of 16 rows and consume pairs on 16x16 products, fp32 caches one row
-// tile and single blocks (pf_piece). Scores and probabilities stay in
-// registers (the FlashAttention principle [P3 §3.4]).
+// of its rows. bf16, fp16 and E4M3 caches (the codes widened exactly to bf16
+// as they are staged) give each wave 32 rows and consume blocks in pairs on
+// 32x32x16 products (pf_piece32); fp32 caches give it one 16-row tile and
+// single blocks (pf_piece). Scores and probabilities stay in registers (the
+// FlashAttention principle [P3 §3.4]).
 //
 // A workgroup's time is its tile's key count, which in a causal chunk grows
 // with the tile's position and with the request's cached context: one
@@ -70,8 +70,8 @@ constexpr int kPfAux = PA_PF_LOAD_AUX;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 static_assert(PA_PREFILL_RING % 4 == 0, "the ring (halved for fp32) alternates two LDS buffers");
 
-// How one workgroup stages a block's head slice (16 keys) in LDS, in the
-// cache's storage type (E4M3 codes stay codes until the operands are built).
+// How one workgroup of the 16-row tile stages a block's head slice (16 keys)
+// in LDS, in the cache's storage type.
 template <class E, int D>
 struct Stage {
   using KS = typename Ops<E, D>::kv_storage;
@@ -115,22 +115,11 @@ __device__ inline int pf_tile_blocks(const AttnArgs& a, const PfRequest& q, int 
   return (kmax + kBlockTokens - 1) / kBlockTokens;
 }
 
-// 16-bit operands are consumed two blocks at a time (consume_pair_tiles)
-// unless PA_PREFILL_PAIRS is 0; fp32 ones block by block.
-#ifndef PA_PREFILL_PAIRS
-#define PA_PREFILL_PAIRS 1
-#endif
-template <class E>
-constexpr bool pf_pairs() {
-  return PA_PREFILL_PAIRS && sizeof(typename E::storage) == 2;
-}
-// Double-buffered LDS copies of the KV blocks' head slices consumed at once
-// (a pair or one block).
+// Double-buffered LDS copies of the KV blocks' head slices (16-row tile).
 template <class E, int D>
 struct PfLds {
-  static constexpr int kBufs = pf_pairs<E>() ? 4 : 2;
-  char k[kBufs][kBlockTokens * Stage<E, D>::kLdsRow];
-  char v[kBufs][kBlockTokens * Stage<E, D>::kLdsRow];
+  char k[2][kBlockTokens * Stage<E, D>::kLdsRow];
+  char v[2][kBlockTokens * Stage<E, D>::kLdsRow];
 };
 
 // One piece: KV blocks [b0, b1) of tile `tile` of request r (rq) for KV
@@ -242,40 +231,19 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
   // (kend), so it adds nothing, and the accumulators stay in one set of
   // registers.
   auto group = [&](int i0, auto masked) {
-    if constexpr (pf_pairs<E>()) {
-      static_assert(RING % 4 == 0, "pairs alternate between two LDS buffer pairs");
 #pragma unroll
-      for (int j = 0; j < RING; j += 2) {
-        const int i = i0 + j;
-        const int b = j & 2;  // this pair's buffers: b, b + 1
-        stage(ring[j], b);
-        stage(ring[j + 1], b + 1);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        issue(ring[j], i + RING);
-        issue(ring[j + 1], i + 1 + RING);
-        __builtin_amdgcn_sched_barrier(0);
-        typename O::KV kv0, kv1;
-        O::load_lds(kv0, lds.k[b], lds.v[b], St::kLdsRow, lane);
-        O::load_lds(kv1, lds.k[b + 1], lds.v[b + 1], St::kLdsRow, lane);
-        consume_pair_tiles<E, D, RT, decltype(masked)::value>(st, kv0, kv1, q, i * kBlockTokens,
-                                                              kend, scale_log2, lane);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < RING; ++j) {
-        const int i = i0 + j;
-        const int buf = j & 1;
-        stage(ring[j], buf);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        issue(ring[j], i + RING);
-        __builtin_amdgcn_sched_barrier(0);
-        typename O::KV kv;
-        O::load_lds(kv, lds.k[buf], lds.v[buf], St::kLdsRow, lane);
-        consume_block_tiles<E, D, RT, decltype(masked)::value>(st, kv, q, i * kBlockTokens, kend,
-                                                               scale_log2, lane);
-      }
+    for (int j = 0; j < RING; ++j) {
+      const int i = i0 + j;
+      const int buf = j & 1;
+      stage(ring[j], buf);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ring[j], i + RING);
+      __builtin_amdgcn_sched_barrier(0);
+      typename O::KV kv;
+      O::load_lds(kv, lds.k[buf], lds.v[buf], St::kLdsRow, lane);
+      consume_block_tiles<E, D, RT, decltype(masked)::value>(st, kv, q, i * kBlockTokens, kend,
+                                                             scale_log2, lane);
     }
   };
   int i0 = b0;
@@ -321,7 +289,8 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
 }
 
 // ------------------------------------------------------------ 32-row tiles
-// 16-bit caches take 32 query rows per wave and a pair of blocks (32 keys)
+// 16-bit operands (16-bit caches, and E4M3 caches widened to bf16 in LDS)
+// take 32 query rows per wave and a pair of blocks (32 keys)
 // per step on 32x32x16 MFMAs. S^T = K.Q^T leaves each lane 16 scores of one
 // query row -- register 4J + I holds key 8J + 4h + I of the pair, h being the
 // lane's half of the wave -- so a row's maximum is 15 in-lane maxima and one
@@ -336,17 +305,17 @@ __device__ inline void pf_piece(const AttnArgs& a, PfLds<E, D>& lds, const PfReq
 // consecutive dims per J.
 template <class E>
 constexpr bool pf32() {
-  return sizeof(typename E::kv_storage) == 2 && sizeof(typename E::storage) == 2;
+  return sizeof(typename E::storage) == 2;
 }
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 template <class E>
 __device__ inline f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (std::is_same<E, Bf16>::value)
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  else
+  if constexpr (std::is_same<E, F16>::value)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else  // bf16, and E4M3 codes widened to bf16
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 template <int D>
 struct T32 {
@@ -382,14 +351,16 @@ struct PfLds32 {
   char v[2][2 * kPf32Pairs][4 * T32<D>::kVQuad];            // [buffer][block][quad][dim][4 keys]
 };
 // One block's staging registers of a thread: a 16-byte K piece, and one dword
-// (two dims) of each of the four keys of a V quad.
+// (two dims, or four E4M3 codes) of each of the four keys of a V quad.
 struct Regs32 {
   u32x4 k;
   u32x4 v;
 };
 
-// As pf_piece, for 16-bit caches with 32 rows per wave (partial rows in tile
-// order: wave * 32 + row).
+// As pf_piece, for 16-bit operands with 32 rows per wave (partial rows in
+// tile order: wave * 32 + row). A 16-bit cache is staged as it is; an E4M3
+// cache's codes are widened exactly to bf16 on their way into LDS, so the
+// LDS layout and everything after it are the bf16 tile's.
 template <class E, int D, int RING>
 __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRequest& rq, int r,
                                   int kvh, int tile, int b0, int b1, int64_t slot) {
@@ -397,6 +368,9 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   using S = typename E::storage;
   using KS = typename E::kv_storage;
   static_assert(RING % 4 == 0, "pairs alternate between two LDS pair buffers");
+  constexpr bool kCodes = sizeof(KS) == 1;  // an E4M3 cache
+  constexpr int kStep = 2 * kPf32Pairs;     // blocks per barrier
+  static_assert(RING % kStep == 0, "whole steps per group");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -447,18 +421,33 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   const KS* v_head = static_cast<const KS*>(a.v_cache) + (int64_t)kvh * D;
   const __attribute__((address_space(4))) int32_t* tab =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)r * a.max_blocks);
-  constexpr int kPiecesPerRow = 2 * D / 16;
+  // Staging items. 16-bit cache: every thread takes item tid of every block
+  // (a 16-byte piece of K: 8 dims of one key; a dword of each of the four
+  // keys of a V quad: 2 dims). E4M3 cache (half the bytes per block): the
+  // threads form kStep groups and group qb stages block qb of each step
+  // alone, item it of it (16 codes of K: 16 dims; 4 codes of each key of a
+  // V quad: 4 dims), so a thread holds one block of the step, not kStep.
+  constexpr int kGroupThreads = kPrefillThreads / kStep;
+  static_assert(!kCodes || kGroupThreads >= D, "one E4M3 staging item per thread and block");
+  const int qb = kCodes ? __builtin_amdgcn_readfirstlane(tid / kGroupThreads) : 0;
+  const int it = kCodes ? tid - qb * kGroupThreads : tid;
+  const bool k_item = kCodes ? it < D : tid < T::kKPieces;
+  const bool v_item = kCodes ? it < D : tid < T::kVItems;
+  constexpr int kPiecesPerRow = D * (int)sizeof(KS) / 16;  // 16-byte pieces of a key's slice
+  constexpr int kVDims = 4 / (int)sizeof(KS);              // dims of one V dword
   // a thread without an item reads past every range: zeros, no memory access
-  const int k_goff = tid < T::kKPieces
-                         ? (tid / kPiecesPerRow) * row_bytes_g + (tid % kPiecesPerRow) * 16
-                         : 0x40000000;
-  const int k_loff = (tid / kPiecesPerRow) * T::kKRow + (tid % kPiecesPerRow) * 16;
-  const int vq = tid / (D / 2), vdp = tid % (D / 2);
-  const int v_goff = tid < T::kVItems ? 4 * vq * row_bytes_g + 4 * vdp : 0x40000000;
-  // entries 2vdp and 2vdp + 1 land in one aligned 16-byte slot, swapped when
-  // the swizzle flips bit 0
-  const int v_loff = vq * T::kVQuad + 8 * (T::vpos(2 * vdp) & ~1);
-  const bool v_swap = (T::vpos(2 * vdp) & 1) != 0;
+  const int k_goff = k_item ? (it / kPiecesPerRow) * row_bytes_g + (it % kPiecesPerRow) * 16
+                            : 0x40000000;
+  const int k_loff = (it / kPiecesPerRow) * T::kKRow + (it % kPiecesPerRow) * 16 * (int)(2 / sizeof(KS));
+  const int vq = it / (D / kVDims), vd = it % (D / kVDims);
+  const int v_goff = v_item ? 4 * vq * row_bytes_g + 4 * vd : 0x40000000;
+  // entries d and d + 1 (d even) land in one aligned 16-byte slot, swapped
+  // when the swizzle flips bit 0; an E4M3 item has two such pairs
+  const int vd0 = kVDims * vd;
+  const int v_loff = vq * T::kVQuad + 8 * (T::vpos(vd0) & ~1);
+  const bool v_swap = (T::vpos(vd0) & 1) != 0;
+  const int v_loff2 = vq * T::kVQuad + 8 * (T::vpos(vd0 + 2) & ~1);
+  const bool v_swap2 = (T::vpos(vd0 + 2) & 1) != 0;
   // Block ids of the loop's loads are read one group ahead by a vector load
   // (lane k: block first + k) and taken from their lanes when used: scalar
   // loads would share the LDS reads' wait counter, and every wait for an LDS
@@ -482,16 +471,40 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
     rg.v.z = buf_load4<kPfAux>(rv, v_goff + 2 * row_bytes_g);
     rg.v.w = buf_load4<kPfAux>(rv, v_goff + 3 * row_bytes_g);
   };
+  // x0 .. x3: two dims d, d + 1 (low, high halves) of keys 4vq .. 4vq + 3,
+  // as the entries (d: 4 keys) and (d + 1: 4 keys) at loff
+  auto put_v_pair = [&](int s, int bsel, unsigned x0, unsigned x1, unsigned x2, unsigned x3,
+                        int loff, bool swap) {
+    const u32x2 e0 = {__builtin_amdgcn_perm(x1, x0, 0x05040100u),
+                      __builtin_amdgcn_perm(x3, x2, 0x05040100u)};
+    const u32x2 e1 = {__builtin_amdgcn_perm(x1, x0, 0x07060302u),
+                      __builtin_amdgcn_perm(x3, x2, 0x07060302u)};
+    const u32x2 first = swap ? e1 : e0, second = swap ? e0 : e1;
+    *reinterpret_cast<u32x4*>(&lds.v[s][bsel][loff]) = u32x4{first.x, first.y, second.x, second.y};
+  };
   auto stage = [&](const Regs32& rg, int s, int bsel) {
-    if (tid < T::kKPieces) *reinterpret_cast<u32x4*>(&lds.k[s][bsel][k_loff]) = rg.k;
-    if (tid < T::kVItems) {
-      // keys 4vq .. 4vq + 3 of dims 2vdp (low halves) and 2vdp + 1 (high halves)
-      const u32x2 e0 = {__builtin_amdgcn_perm(rg.v.y, rg.v.x, 0x05040100u),
-                        __builtin_amdgcn_perm(rg.v.w, rg.v.z, 0x05040100u)};
-      const u32x2 e1 = {__builtin_amdgcn_perm(rg.v.y, rg.v.x, 0x07060302u),
-                        __builtin_amdgcn_perm(rg.v.w, rg.v.z, 0x07060302u)};
-      const u32x2 first = v_swap ? e1 : e0, second = v_swap ? e0 : e1;
-      *reinterpret_cast<u32x4*>(&lds.v[s][bsel][v_loff]) = u32x4{first.x, first.y, second.x, second.y};
+    if constexpr (kCodes) {
+      if (it < D) {
+        // every E4M3 value is a bf16 value: exact widening
+        unsigned w[8];
+        fp8x4_to_bf16(rg.k.x, &w[0], &w[1]);
+        fp8x4_to_bf16(rg.k.y, &w[2], &w[3]);
+        fp8x4_to_bf16(rg.k.z, &w[4], &w[5]);
+        fp8x4_to_bf16(rg.k.w, &w[6], &w[7]);
+        char* kd = &lds.k[s][bsel][k_loff];
+        *reinterpret_cast<u32x4*>(kd) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(kd + 16) = u32x4{w[4], w[5], w[6], w[7]};
+        unsigned lo[4], hi[4];  // key i: dims vd0, vd0 + 1 and vd0 + 2, vd0 + 3
+        fp8x4_to_bf16(rg.v.x, &lo[0], &hi[0]);
+        fp8x4_to_bf16(rg.v.y, &lo[1], &hi[1]);
+        fp8x4_to_bf16(rg.v.z, &lo[2], &hi[2]);
+        fp8x4_to_bf16(rg.v.w, &lo[3], &hi[3]);
+        put_v_pair(s, bsel, lo[0], lo[1], lo[2], lo[3], v_loff, v_swap);
+        put_v_pair(s, bsel, hi[0], hi[1], hi[2], hi[3], v_loff2, v_swap2);
+      }
+    } else {
+      if (k_item) *reinterpret_cast<u32x4*>(&lds.k[s][bsel][k_loff]) = rg.k;
+      if (v_item) put_v_pair(s, bsel, rg.v.x, rg.v.y, rg.v.z, rg.v.w, v_loff, v_swap);
     }
   };
 
@@ -583,11 +596,15 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   };
 
   int nid = load_ids(b0 + RING);  // lane k: the id of the block the group's load k reads
-  Regs32 ring[RING];
+  // the blocks of a group this thread stages: all RING, or (E4M3) block qb
+  // of each of its RING / kStep steps
+  constexpr int kMine = kCodes ? RING / kStep : RING;
+  Regs32 ring[kMine];
 #pragma unroll
-  for (int jj = 0; jj < RING; ++jj) {
+  for (int m = 0; m < kMine; ++m) {
+    const int jj = kCodes ? m * kStep + qb : m;
     const int li = min(b0 + jj, b1 - 1);
-    issue(ring[jj], b0 + jj, block16(tab[li >> a.block_shift], li, a.block_shift, a.num_blocks));
+    issue(ring[m], b0 + jj, block16(tab[li >> a.block_shift], li, a.block_shift, a.num_blocks));
   }
   // take the ids in here (a wait for the one load issued before the ring's):
   // entering the loop with the load still pending makes the compiler wait
@@ -599,21 +616,27 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   // every row's limit (kend), so it adds nothing.
   // With kPf32Pairs == 2 a group is one step of 4 blocks and the LDS buffer
   // alternates between groups.
-  constexpr int kStep = 2 * kPf32Pairs;  // blocks per barrier
-  static_assert(RING % kStep == 0, "whole steps per group");
   auto group = [&](int i0, auto masked) {
     const int nxt = load_ids(i0 + 2 * RING);
 #pragma unroll
     for (int jj = 0; jj < RING; jj += kStep) {
       const int i = i0 + jj;
       const int s = RING / kStep >= 2 ? (jj / kStep) & 1 : ((i - b0) / kStep) & 1;
+      if constexpr (kCodes) {
+        stage(ring[jj / kStep], s, qb);
+      } else {
 #pragma unroll
-      for (int bb = 0; bb < kStep; ++bb) stage(ring[jj + bb], s, bb);
+        for (int bb = 0; bb < kStep; ++bb) stage(ring[jj + bb], s, bb);
+      }
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kCodes) {
+        issue(ring[jj / kStep], i + qb + RING, __builtin_amdgcn_readlane(nid, jj + qb));
+      } else {
 #pragma unroll
-      for (int bb = 0; bb < kStep; ++bb)
-        issue(ring[jj + bb], i + bb + RING, __builtin_amdgcn_readlane(nid, jj + bb));
+        for (int bb = 0; bb < kStep; ++bb)
+          issue(ring[jj + bb], i + bb + RING, __builtin_amdgcn_readlane(nid, jj + bb));
+      }
       __builtin_amdgcn_sched_barrier(0);
       f32x16 acc[kPf32Pairs];
 #pragma unroll
