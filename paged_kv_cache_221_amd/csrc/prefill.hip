@@ -345,6 +345,11 @@ static_assert(kPrefillWaves * kWave >= T32<128>::kKPieces && kPrefillWaves * kWa
 #define PA_PF32_PAIRS 2
 #endif
 constexpr int kPf32Pairs = PA_PF32_PAIRS;
+// Thread groups that share the staging of a step's blocks on a 16-bit cache
+// (1: every thread < 2 D stages a piece of every block).
+#ifndef PA_PF32_STAGE_GROUPS
+#define PA_PF32_STAGE_GROUPS 1
+#endif
 template <int D>
 struct PfLds32 {
   char k[2][2 * kPf32Pairs][kBlockTokens * T32<D>::kKRow];  // [buffer][block][key row]
@@ -421,18 +426,22 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   const KS* v_head = static_cast<const KS*>(a.v_cache) + (int64_t)kvh * D;
   const __attribute__((address_space(4))) int32_t* tab =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)r * a.max_blocks);
-  // Staging items. 16-bit cache: every thread takes item tid of every block
-  // (a 16-byte piece of K: 8 dims of one key; a dword of each of the four
-  // keys of a V quad: 2 dims). E4M3 cache (half the bytes per block): the
-  // threads form kStep groups and group qb stages block qb of each step
-  // alone, item it of it (16 codes of K: 16 dims; 4 codes of each key of a
-  // V quad: 4 dims), so a thread holds one block of the step, not kStep.
-  constexpr int kGroupThreads = kPrefillThreads / kStep;
-  static_assert(!kCodes || kGroupThreads >= D, "one E4M3 staging item per thread and block");
-  const int qb = kCodes ? __builtin_amdgcn_readfirstlane(tid / kGroupThreads) : 0;
-  const int it = kCodes ? tid - qb * kGroupThreads : tid;
-  const bool k_item = kCodes ? it < D : tid < T::kKPieces;
-  const bool v_item = kCodes ? it < D : tid < T::kVItems;
+  // Staging items: the threads form kGroups groups and group qb stages
+  // blocks qb * kPer .. qb * kPer + kPer - 1 of each step, item `it` of each.
+  // An item is a 16-byte piece of K (16-bit cache: 8 dims of one key; E4M3:
+  // 16 codes, 16 dims) and a dword of each of the four keys of a V quad (2
+  // dims, or 4 codes). E4M3 blocks are half the bytes, so every group takes
+  // one block per step; 16-bit caches take PA_PF32_STAGE_GROUPS groups.
+  constexpr int kGroups = kCodes ? kStep : PA_PF32_STAGE_GROUPS;
+  static_assert(kStep % kGroups == 0, "whole blocks per staging group");
+  constexpr int kPer = kStep / kGroups;                  // blocks of a step per thread
+  constexpr int kGroupThreads = kPrefillThreads / kGroups;
+  constexpr int kItems = kCodes ? D : T::kKPieces;       // items per block (K pieces = V items)
+  static_assert(kCodes || T::kKPieces == T::kVItems, "one K piece and one V item per staging item");
+  static_assert(kGroupThreads >= kItems, "one staging item per thread and block");
+  const int qb = kGroups > 1 ? __builtin_amdgcn_readfirstlane(tid / kGroupThreads) : 0;
+  const int it = tid - qb * kGroupThreads;
+  const bool k_item = it < kItems, v_item = it < kItems;
   constexpr int kPiecesPerRow = D * (int)sizeof(KS) / 16;  // 16-byte pieces of a key's slice
   constexpr int kVDims = 4 / (int)sizeof(KS);              // dims of one V dword
   // a thread without an item reads past every range: zeros, no memory access
@@ -596,13 +605,13 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   };
 
   int nid = load_ids(b0 + RING);  // lane k: the id of the block the group's load k reads
-  // the blocks of a group this thread stages: all RING, or (E4M3) block qb
-  // of each of its RING / kStep steps
-  constexpr int kMine = kCodes ? RING / kStep : RING;
+  // the blocks of a group this thread stages: its kPer blocks of each of the
+  // group's RING / kStep steps (ring slot (step, bb) = step * kPer + bb)
+  constexpr int kMine = RING / kStep * kPer;
   Regs32 ring[kMine];
 #pragma unroll
   for (int m = 0; m < kMine; ++m) {
-    const int jj = kCodes ? m * kStep + qb : m;
+    const int jj = (m / kPer) * kStep + qb * kPer + m % kPer;
     const int li = min(b0 + jj, b1 - 1);
     issue(ring[m], b0 + jj, block16(tab[li >> a.block_shift], li, a.block_shift, a.num_blocks));
   }
@@ -622,20 +631,14 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
     for (int jj = 0; jj < RING; jj += kStep) {
       const int i = i0 + jj;
       const int s = RING / kStep >= 2 ? (jj / kStep) & 1 : ((i - b0) / kStep) & 1;
-      if constexpr (kCodes) {
-        stage(ring[jj / kStep], s, qb);
-      } else {
 #pragma unroll
-        for (int bb = 0; bb < kStep; ++bb) stage(ring[jj + bb], s, bb);
-      }
+      for (int bb = 0; bb < kPer; ++bb) stage(ring[jj / kStep * kPer + bb], s, qb * kPer + bb);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kCodes) {
-        issue(ring[jj / kStep], i + qb + RING, __builtin_amdgcn_readlane(nid, jj + qb));
-      } else {
 #pragma unroll
-        for (int bb = 0; bb < kStep; ++bb)
-          issue(ring[jj + bb], i + bb + RING, __builtin_amdgcn_readlane(nid, jj + bb));
+      for (int bb = 0; bb < kPer; ++bb) {
+        const int blk = qb * kPer + bb;  // this thread's block of the step
+        issue(ring[jj / kStep * kPer + bb], i + blk + RING, __builtin_amdgcn_readlane(nid, jj + blk));
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x16 acc[kPf32Pairs];
