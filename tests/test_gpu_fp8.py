@@ -221,7 +221,8 @@ def test_fp8_sweep(gpu_lib, seed):
     varlen step on the mixed one, against the oracle over dequantised values.
     PA_SWEEP_SEEDS=n runs n cases."""
     rng = np.random.Generator(np.random.PCG64(8800 + seed))
-    hq, hkv, d = [(32, 8, 128), (16, 4, 64), (8, 8, 128), (16, 2, 128)][seed % 4]
+    hq, hkv, d = [(32, 8, 128), (16, 4, 64), (8, 8, 128), (16, 2, 128), (16, 1, 64),
+                  (8, 4, 128)][seed % 6]
     bs = [16, 32, 16, 64, 256][seed % 5]
     ks, vs = float(rng.choice([0.02, 0.0625, 0.2])), float(rng.choice([0.03, 0.05, 0.125]))
     b = int(rng.choice([1, 3, 9, 40]))

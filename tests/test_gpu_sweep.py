@@ -25,7 +25,8 @@ from _parity import (check_cache_after_write, check_close, decode_oracle, gpu_ro
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(32, 8, 128), (16, 4, 64), (8, 2, 128), (16, 16, 128), (8, 1, 64), (64, 8, 128)]
+SHAPES = [(32, 8, 128), (16, 4, 64), (8, 2, 128), (16, 16, 128), (8, 1, 64), (64, 8, 128),
+          (32, 2, 128), (16, 8, 64)]
 # cache block sizes drawn per case (16 most often)
 BLOCKS = [16, 16, 32, 16, 64, 256]
 # PA_SWEEP_SEEDS=n runs n cases per sweep instead of the default counts
