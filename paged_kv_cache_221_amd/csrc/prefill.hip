@@ -350,6 +350,15 @@ constexpr int kPf32Pairs = PA_PF32_PAIRS;
 #ifndef PA_PF32_STAGE_GROUPS
 #define PA_PF32_STAGE_GROUPS 1
 #endif
+// Whether a step's blocks are staged in LDS in the middle of the previous
+// step (1) or at its own start, right before its barrier (0), for E4M3 and
+// for 16-bit caches.
+#ifndef PA_PF32_MIDSTAGE_CODES
+#define PA_PF32_MIDSTAGE_CODES 1
+#endif
+#ifndef PA_PF32_MIDSTAGE_16
+#define PA_PF32_MIDSTAGE_16 0
+#endif
 template <int D>
 struct PfLds32 {
   char k[2][2 * kPf32Pairs][kBlockTokens * T32<D>::kKRow];  // [buffer][block][key row]
@@ -604,6 +613,18 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
     }
   };
 
+  // Two stagings. Either each step's blocks are staged right before its
+  // barrier (16-bit caches), or step k's blocks (LDS buffer k & 1) are
+  // staged in the middle of step k - 1, once its score products are issued
+  // (E4M3 caches, whose staging every wave shares): every wave passed step
+  // k - 1's barrier after its last reads of that buffer (step k - 2), so it
+  // is free, and the LDS writes, which queue behind the other waves' operand
+  // reads, have the rest of the step to finish. Either way a step's loads
+  // are issued one step ahead of its staging. Measured on the mixed step's
+  // chunks: E4M3 mid-step 109-111 us against 112-114; 16-bit caches, whose
+  // staging falls on waves 0-3 alone, 119 us against 112-113.
+  constexpr bool kMid = kCodes ? PA_PF32_MIDSTAGE_CODES : PA_PF32_MIDSTAGE_16;
+  static_assert(!kMid || RING == kStep, "mid-step staging: one step of blocks in flight");
   int nid = load_ids(b0 + RING);  // lane k: the id of the block the group's load k reads
   // the blocks of a group this thread stages: its kPer blocks of each of the
   // group's RING / kStep steps (ring slot (step, bb) = step * kPer + bb)
@@ -614,6 +635,17 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
     const int jj = (m / kPer) * kStep + qb * kPer + m % kPer;
     const int li = min(b0 + jj, b1 - 1);
     issue(ring[m], b0 + jj, block16(tab[li >> a.block_shift], li, a.block_shift, a.num_blocks));
+  }
+  if constexpr (kMid) {
+    // step 0 into buffer 0, then step 1's loads
+#pragma unroll
+    for (int bb = 0; bb < kPer; ++bb) stage(ring[bb], 0, qb * kPer + bb);
+#pragma unroll
+    for (int bb = 0; bb < kPer; ++bb) {
+      const int blk = qb * kPer + bb;  // this thread's block of the step
+      issue(ring[bb], b0 + RING + blk, __builtin_amdgcn_readlane(nid, blk));
+    }
+    nid = load_ids(b0 + 2 * RING);  // ids of step 2
   }
   // take the ids in here (a wait for the one load issued before the ring's):
   // entering the loop with the load still pending makes the compiler wait
@@ -626,29 +658,53 @@ __device__ inline void pf_piece32(const AttnArgs& a, PfLds32<D>& lds, const PfRe
   // With kPf32Pairs == 2 a group is one step of 4 blocks and the LDS buffer
   // alternates between groups.
   auto group = [&](int i0, auto masked) {
-    const int nxt = load_ids(i0 + 2 * RING);
-#pragma unroll
-    for (int jj = 0; jj < RING; jj += kStep) {
-      const int i = i0 + jj;
-      const int s = RING / kStep >= 2 ? (jj / kStep) & 1 : ((i - b0) / kStep) & 1;
-#pragma unroll
-      for (int bb = 0; bb < kPer; ++bb) stage(ring[jj / kStep * kPer + bb], s, qb * kPer + bb);
+    if constexpr (kMid) {
+      const int s = ((i0 - b0) / kStep) & 1;
       __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int bb = 0; bb < kPer; ++bb) {
-        const int blk = qb * kPer + bb;  // this thread's block of the step
-        issue(ring[jj / kStep * kPer + bb], i + blk + RING, __builtin_amdgcn_readlane(nid, jj + blk));
-      }
       __builtin_amdgcn_sched_barrier(0);
       f32x16 acc[kPf32Pairs];
 #pragma unroll
       for (int pp = 0; pp < kPf32Pairs; ++pp) acc[pp] = qk(s, pp);
+      __builtin_amdgcn_sched_barrier(0);
+      const int nxt = load_ids(i0 + 3 * RING);
+#pragma unroll
+      for (int bb = 0; bb < kPer; ++bb) stage(ring[bb], s ^ 1, qb * kPer + bb);
+#pragma unroll
+      for (int bb = 0; bb < kPer; ++bb) {
+        const int blk = qb * kPer + bb;
+        issue(ring[bb], i0 + 2 * RING + blk, __builtin_amdgcn_readlane(nid, blk));
+      }
+      __builtin_amdgcn_sched_barrier(0);
       float pr[kPf32Pairs][16];
-      const float alpha = softmax(acc, i * kBlockTokens, pr, masked);
+      const float alpha = softmax(acc, i0 * kBlockTokens, pr, masked);
       accumulate(pr, alpha, s);
+      nid = nxt;
+    } else {
+      const int nxt = load_ids(i0 + 2 * RING);
+#pragma unroll
+      for (int jj = 0; jj < RING; jj += kStep) {
+        const int i = i0 + jj;
+        const int s = RING / kStep >= 2 ? (jj / kStep) & 1 : ((i - b0) / kStep) & 1;
+#pragma unroll
+        for (int bb = 0; bb < kPer; ++bb) stage(ring[jj / kStep * kPer + bb], s, qb * kPer + bb);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int bb = 0; bb < kPer; ++bb) {
+          const int blk = qb * kPer + bb;  // this thread's block of the step
+          issue(ring[jj / kStep * kPer + bb], i + blk + RING,
+                __builtin_amdgcn_readlane(nid, jj + blk));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 acc[kPf32Pairs];
+#pragma unroll
+        for (int pp = 0; pp < kPf32Pairs; ++pp) acc[pp] = qk(s, pp);
+        float pr[kPf32Pairs][16];
+        const float alpha = softmax(acc, i * kBlockTokens, pr, masked);
+        accumulate(pr, alpha, s);
+      }
+      nid = nxt;
     }
-    nid = nxt;
   };
   int i0 = b0;
   for (; i0 + RING <= b_full; i0 += RING) group(i0, std::false_type{});
