@@ -175,6 +175,34 @@ def test_fp8_prefill_chunks(gpu_lib, case, path):
                 label=f"{lay.name} e4m3 prefill {path}")
 
 
+@pytest.mark.parametrize("variant", ["non-causal", "negative-scale", "zero-scale"])
+@pytest.mark.parametrize("shape", [(128, 16, 2), (64, 16, 16)], ids=lambda c: "-".join(map(str, c)))
+def test_fp8_prefill_mask_and_scale_variants(gpu_lib, variant, shape):
+    """E4M3 prefill chunks with every key visible (no causal mask), and with
+    a negative or a zero softmax scale (a negative one is applied to -q on
+    the blocks every row sees whole; zero gives the mean of the visible
+    values), on both prefill kernels, for GQA groups 8 and 1."""
+    d, hq, hkv = shape
+    lay = small_varlen(1010 + d + hkv, dtype="bf16", num_heads=hq, num_kv_heads=hkv,
+                       head_dim=d, prefill=((70, 200), (33, 0), (129, 40)), decode_lens=(1, 90))
+    s = _Fp8Step(lay, 0.0625, 0.05)
+    s.write()
+    st = s.st
+    causal = variant != "non-causal"
+    scale = {"non-causal": 1.0, "negative-scale": -1.0, "zero-scale": 0.0}[variant] * lay.scale
+    want, _ = oracle.paged_varlen(s.q, s.k, s.v, lay.cu_seqlens_q, lay.seq_lens,
+                                  lay.block_table, scale, lay.block_size, "bf16", causal=causal,
+                                  kv_dtype="e4m3", k_scale=s.ks, v_scale=s.vs)
+    for ws in ("auto", None):
+        out = pa.pa_varlen(st.k_cache, st.v_cache, st.q, st.cu_seqlens_q, st.seq_lens,
+                           st.block_table, lay.max_query_len, lay.max_seq_len, scale,
+                           causal=causal, workspace=ws, **s.kw())
+        torch.cuda.synchronize()
+        check_close(gpu_rows(out, "bf16"), want, "bf16",
+                    groups=request_groups(lay, range(lay.num_seqs)),
+                    label=f"{lay.name} e4m3 {variant} workspace={ws}")
+
+
 @pytest.mark.parametrize("bs", [32, 256])
 def test_fp8_cache_blocks_larger_than_16(gpu_lib, bs):
     """An E4M3 cache with 32- or 256-token blocks: the balanced decode, the
