@@ -410,7 +410,8 @@ def read_ceiling(copies, layout, k: int):
 SECONDARY_LEGS = ("tiny-decode-fp32", "long-context-splitk-bf16", "llama2-7b-mha-decode-fp16",
                   "mixed-step-bf16", "mixed-step-prefill-chunks-bf16",
                   "mixed-step-prefill-chunks-e4m3-cache", "mixed-step-e4m3-cache",
-                  "llama3-8b-decode-e4m3-cache", "llama3-8b-spec-verify-q4-bf16",
+                  "llama3-8b-decode-e4m3-cache", "long-context-splitk-e4m3-cache",
+                  "llama3-8b-spec-verify-q4-bf16",
                   "rope-write-kv-mixed-step-bf16", "copy-on-write-blocks-bf16",
                   "block-manager-host")
 
@@ -506,6 +507,7 @@ def secondary(args, only=None):
                       ("mixed-step-prefill-chunks-e4m3-cache", bench_prefill_only_fp8),
                       ("mixed-step-e4m3-cache", bench_mixed_fp8),
                       ("llama3-8b-decode-e4m3-cache", bench_fp8_decode),
+                      ("long-context-splitk-e4m3-cache", bench_splitk_fp8),
                       ("llama3-8b-spec-verify-q4-bf16", bench_spec_verify),
                       ("rope-write-kv-mixed-step-bf16", bench_rope_write),
                       ("copy-on-write-blocks-bf16", bench_copy_blocks)):
@@ -633,6 +635,31 @@ def bench_mixed_fp8(k: int):
     res["cpu_oracle"] = oracle_sample(st, lay, [1] + dec[:4], "varlen",
                                       kv=dict(dtype="e4m3", k_scale=ks, v_scale=vs))
     del st, out, ws, write, attn
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_splitk_fp8(k: int):
+    """The long-context batch (8 requests of 32k-128k tokens) on an E4M3
+    cache: write, then split-K partials and the LSE merge (bf16 q and
+    output). Algorithmic bytes as the bf16 leg's with one byte per cached
+    K/V element."""
+    import torch
+    from workloads import long_context_splitk
+    from workloads.tensors import materialize_e4m3
+    lay = long_context_splitk()
+    scales = (0.0625, 0.0625)
+    st = materialize_e4m3(lay, "cuda", *scales, poison=False)
+    step = DecodeStep(st, "splitk", lay.split_tokens, kv_scales=scales)
+    ms, _, kern = time_steps([step], max(k, 10), 3, True)
+    nbytes = decode_bytes(lay, kv_elem_bytes=1)
+    print(f"[bench] long-context split-K (e4m3): attention median "
+          f"{statistics.median(kern):.4f} ms", file=sys.stderr, flush=True)
+    res = timed_leg(nbytes, kern, ms, {"includes": "split-K partials and the LSE merge"})
+    res["cpu_oracle"] = oracle_sample(st, lay, [0], "decode",
+                                      kv=dict(dtype="e4m3", k_scale=scales[0],
+                                              v_scale=scales[1]))
+    del st, step
     torch.cuda.empty_cache()
     return res
 

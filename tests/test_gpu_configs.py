@@ -183,6 +183,33 @@ def test_long_context_splitk_all_requests():
 
 
 @pytest.mark.timeout(900)
+def test_long_context_splitk_e4m3_all_requests():
+    """The long-context batch on an E4M3 cache (the bench's scales; the 1% of
+    keys scaled x8 saturate at the largest code): all eight requests through
+    split-K partials and the LSE merge, against the oracle over the
+    dequantised codes the write left."""
+    lay = long_context_splitk()
+    ks, vs = E4M3_SCALES
+    st = materialize_e4m3(lay, "cuda", ks, vs)
+    pa.pa_write_kv(st.k_cache, st.v_cache, st.k_new, st.v_new, st.slot_mapping,
+                   k_scale=ks, v_scale=vs)
+    o, l = pa.pa_decode_splitk(st.k_cache, st.v_cache, st.q, st.block_table, st.seq_lens,
+                               lay.max_seq_len, lay.split_tokens, lay.scale, k_scale=ks,
+                               v_scale=vs)
+    out, lse = pa.pa_lse_merge(o, l, st.seq_lens, lay.max_seq_len, lay.split_tokens,
+                               out_dtype=torch.bfloat16, want_lse=True)
+    torch.cuda.synchronize()
+    req = list(range(lay.num_seqs))
+    want, want_lse = oracle.paged_decode(raw_bits(st.q, "bf16"), raw_bits(st.k_cache, "e4m3"),
+                                         raw_bits(st.v_cache, "e4m3"), lay.block_table,
+                                         lay.seq_lens, lay.scale, lay.block_size, "bf16",
+                                         requests=req, kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    check_close(gpu_rows(out, "bf16"), want, "bf16",
+                label=f"{lay.name} e4m3 split-K + merge: {len(req)} requests")
+    assert max_err(lse.cpu().double().numpy(), want_lse) <= TOL["bf16"]
+
+
+@pytest.mark.timeout(900)
 def test_long_context_balanced_all_requests():
     lay = long_context_splitk()
     st = materialize(lay, "cuda")
